@@ -1,0 +1,211 @@
+"""Oracle for the hybrid MoE layer: tier map, routing, grouping, align, expert
+MLP and the shared top-k weighted sum.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring for who may import this).
+
+Pages (cited by title and section):
+* local-inference-lab/vllm PR #92 "quant: nvfp4_nf3_hybrid", "How it works":
+  two prepared weight objects per layer (one per tier), both launches share one
+  route geometry and one top-k sum, the second accumulates into the first; an
+  M <= 8 decode path addressed directly by the top-k result; layers absent from
+  the bit map run uniform NVFP4.
+* PR #104 description: bit map values 4 = kept tier, 3 = NF3; the kept format
+  may switch the kept tier to MXFP4; expert weights are demultiplexed into
+  compact tier-local storage.
+Routing (softmax over the router logits, top-k, renormalised) and SwiGLU
+experts are the layer's definition where the pages do not spell them out.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats as F
+
+KEPT, NF3 = 0, 1
+
+
+# ----------------------------------------------------------------------------
+# tier map (global expert id -> tier, tier-local id)
+# ----------------------------------------------------------------------------
+
+def tier_map(bit_map, E: int):
+    """tier[e] = 0 for the kept tier (bit 4, or no bit map at all), 1 for NF3
+    (bit 3); local[e] = number of experts e' < e in the same tier, i.e. the
+    position of e in its tier's ascending-id storage."""
+    tier = np.zeros(E, dtype=np.int32)
+    if bit_map is not None:
+        bm = np.asarray(bit_map)
+        if bm.shape != (E,) or not np.all((bm == 3) | (bm == 4)):
+            raise ValueError("bit map must hold E entries, each 3 or 4")
+        tier = np.where(bm == 3, NF3, KEPT).astype(np.int32)
+    local = np.zeros(E, dtype=np.int32)
+    seen = [0, 0]
+    for e in range(E):
+        local[e] = seen[tier[e]]
+        seen[tier[e]] += 1
+    return tier, local
+
+
+# ----------------------------------------------------------------------------
+# routing
+# ----------------------------------------------------------------------------
+
+def route(logits: np.ndarray, top_k: int):
+    """Softmax top-k, renormalised. Experts are ranked by logit, descending,
+    ties to the lower expert id (a stable sort of the negated logits); the
+    weights are the softmax over the selected logits (equal to softmax over all
+    experts, then top-k, then renormalise), computed in fp64."""
+    L = np.asarray(logits, dtype=np.float32)
+    ids = np.argsort(-L, axis=1, kind="stable")[:, :top_k].astype(np.int32)
+    sel = np.take_along_axis(L, ids, axis=1).astype(np.float64)
+    ex = np.exp(sel - sel[:, :1])
+    w = ex / ex.sum(axis=1, keepdims=True)
+    return ids, w
+
+
+# ----------------------------------------------------------------------------
+# decode grouping (M <= 8): distinct experts and their slots
+# ----------------------------------------------------------------------------
+
+def decode_groups(ids: np.ndarray, tier: np.ndarray, local: np.ndarray):
+    """Distinct experts touched by the top-k result, ordered by (tier, local id),
+    each with its slots s = t * k + j in ascending order."""
+    flat = np.asarray(ids).reshape(-1)
+    experts = sorted(set(int(e) for e in flat), key=lambda e: (int(tier[e]), int(local[e])))
+    return [(e, int(tier[e]), int(local[e]), [s for s in range(flat.size) if flat[s] == e])
+            for e in experts]
+
+
+# ----------------------------------------------------------------------------
+# align (M > 8): per tier, slots sorted by expert and padded to BM
+# ----------------------------------------------------------------------------
+
+def align(ids: np.ndarray, tier: np.ndarray, local: np.ndarray, block_m: int):
+    """Per tier: every slot of that tier's experts, grouped by tier-local expert
+    in ascending local id, ascending slot order inside an expert, each expert's
+    run padded with the sentinel M*k up to a multiple of block_m. Returns, per
+    tier, sorted_slots[num_padded], block_expert[num_padded / block_m],
+    expert_off[E_tier + 1] and num_padded."""
+    flat = np.asarray(ids).reshape(-1)
+    sentinel = flat.size
+    out = []
+    for t in (KEPT, NF3):
+        members = [e for e in range(tier.size) if tier[e] == t]   # ascending = local order
+        offs = [0]
+        sorted_slots = []
+        block_expert = []
+        for e in members:
+            slots = [s for s in range(flat.size) if flat[s] == e]
+            n = len(slots)
+            padded = -(-n // block_m) * block_m
+            sorted_slots += slots + [sentinel] * (padded - n)
+            block_expert += [int(local[e])] * (padded // block_m)
+            offs.append(offs[-1] + padded)
+        out.append({
+            "sorted_slots": np.array(sorted_slots, dtype=np.int32),
+            "block_expert": np.array(block_expert, dtype=np.int32),
+            "expert_off": np.array(offs, dtype=np.int32),
+            "num_padded": int(offs[-1]),
+        })
+    return out
+
+
+# ----------------------------------------------------------------------------
+# dequantised expert weights
+# ----------------------------------------------------------------------------
+
+def expert_weights(layer: dict, e: int):
+    """fp32 dequantised (W13 [2I, H], W2 [H, I]) of global expert e."""
+    tier, local = tier_map(layer["bit_map"], layer["E"])
+    j = int(local[e])
+    if tier[e] == KEPT:
+        k = layer["kept"]
+        if layer["kept_format"] == "nvfp4" or layer["bit_map"] is None:
+            w13 = F.nvfp4_dequant(k["w13_q"][j], k["w13_s"][j], k["w13_g"][j])
+            w2 = F.nvfp4_dequant(k["w2_q"][j], k["w2_s"][j], k["w2_g"][j])
+        else:
+            w13 = F.mxfp4_dequant(k["w13_q"][j], k["w13_s"][j])
+            w2 = F.mxfp4_dequant(k["w2_q"][j], k["w2_s"][j])
+    else:
+        n = layer["nf3"]
+        w13 = F.nf3_dequant(n["w13_q"][j], n["w13_s"][j])
+        w2 = F.nf3_dequant(n["w2_q"][j], n["w2_s"][j])
+    return w13, w2
+
+
+def kept_format_of(layer: dict) -> str:
+    """A layer with no bit map runs uniform NVFP4 whatever the kept format says."""
+    return "nvfp4" if layer["bit_map"] is None else layer["kept_format"]
+
+
+# ----------------------------------------------------------------------------
+# expert MLP and the layer
+# ----------------------------------------------------------------------------
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_mlp(x: np.ndarray, w13: np.ndarray, w2: np.ndarray):
+    """SwiGLU expert: a = W1 x (gate rows), b = W3 x (up rows), h = silu(a) * b,
+    o = W2 h. x is [n, H]; computed in fp64 from the fp32 weights."""
+    I = w2.shape[1]
+    z = x @ w13.astype(np.float64).T
+    h = silu(z[:, :I]) * z[:, I:]
+    return h, h @ w2.astype(np.float64).T
+
+
+def forward(layer: dict, x_bits: np.ndarray, logits: np.ndarray, tokens=None):
+    """The layer: route once, run every selected (token, expert) pair through
+    the expert's MLP in its own tier, and add the outputs into one top-k
+    weighted sum y[t] = sum_j w[t, j] * o[t, j]. `tokens` restricts the
+    returned rows to a subset (the routing result is still for every token).
+    Returns ids, weights, per-slot h (only for the computed tokens) and y
+    (fp64, one row per computed token)."""
+    E, k = layer["E"], layer["top_k"]
+    ids, w = route(logits, k)
+    M = ids.shape[0]
+    tokens = list(range(M)) if tokens is None else list(tokens)
+    x = F.bf16_value(np.asarray(x_bits)[tokens]).astype(np.float64)
+    H, I = layer["H"], layer["I"]
+    y = np.zeros((len(tokens), H), dtype=np.float64)
+    h_all = {}
+    sel = ids[tokens]
+    for e in sorted(set(int(v) for v in sel.reshape(-1))):
+        rows, cols = np.nonzero(sel == e)
+        w13, w2 = expert_weights(layer, e)
+        h, o = expert_mlp(x[rows], w13, w2)
+        y[rows] += w[np.asarray(tokens)[rows], cols][:, None] * o
+        for r, c, hh in zip(rows, cols, h):
+            h_all[int(tokens[r]) * k + int(c)] = hh
+    return {"ids": ids, "w": w, "h": h_all, "y": y, "tokens": tokens}
+
+
+# ----------------------------------------------------------------------------
+# quantising a whole layer from master weights (synthetic inputs only)
+# ----------------------------------------------------------------------------
+
+def quantize_layer(E: int, H: int, I: int, top_k: int, bit_map, kept_format: str, master):
+    """Pack every expert of a layer in its tier with the oracle quantisers.
+    `master(e)` returns the fp32 (W13 [2I, H], W2 [H, I]) of expert e."""
+    from synth import empty_packed_layer
+    layer = empty_packed_layer(E, H, I, top_k, kept_format, bit_map)
+    tier, local = tier_map(bit_map, E)
+    fmt = "nvfp4" if bit_map is None else kept_format
+    for e in range(E):
+        w13, w2 = master(e)
+        j = int(local[e])
+        if tier[e] == KEPT:
+            d = layer["kept"]
+            if fmt == "nvfp4":
+                d["w13_q"][j], d["w13_s"][j], d["w13_g"][j] = F.nvfp4_quantize(w13)
+                d["w2_q"][j], d["w2_s"][j], d["w2_g"][j] = F.nvfp4_quantize(w2)
+            else:
+                d["w13_q"][j], d["w13_s"][j] = F.mxfp4_quantize(w13)
+                d["w2_q"][j], d["w2_s"][j] = F.mxfp4_quantize(w2)
+                d["w13_g"][j] = d["w2_g"][j] = np.float32(1.0)
+        else:
+            d = layer["nf3"]
+            d["w13_q"][j], d["w13_s"][j] = F.nf3_quantize(w13)
+            d["w2_q"][j], d["w2_s"][j] = F.nf3_quantize(w2)
+    return layer
