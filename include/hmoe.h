@@ -1,0 +1,255 @@
+/*
+ * hmoe.h - C ABI of the hybrid-precision W4A16 fused MoE layer for AMD MI355X (gfx950).
+ *
+ * One MoE layer whose experts each live in one of two weight tiers, chosen per
+ * expert by a bit map (4 = kept tier, 3 = NF3 tail). The kept tier is NVFP4
+ * (E2M1 values, an E4M3 scale per 16 along K, an fp32 per-tensor scale) or, when
+ * the kept format says so, MXFP4 (E2M1 values, an E8M0 scale per 32). The NF3
+ * tail stores 3-bit NormalFloat codes with an fp16 absmax scale per 64 along K.
+ * Tokens are bf16, routing is softmax top-k renormalised, the experts are SwiGLU
+ * MLPs, and both tiers add into one shared top-k weighted sum.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] local-inference-lab/vllm PR #92 "quant: nvfp4_nf3_hybrid", "How it works":
+ *        two prepared weight objects per layer, launches sharing one route geometry
+ *        and one top-k sum, the second accumulating into the first, graph-safe, an
+ *        M <= 8 decode path addressed by the top-k result, layers absent from the map
+ *        run uniform NVFP4, no environment variables, scratch sized from the maximum
+ *        number of batched tokens.
+ *   [P2] local-inference-lab/vllm PR #104, description and "Summary": bit map values
+ *        4 = kept, 3 = NF3; a kept format that may switch the kept tier to MXFP4;
+ *        expert weights demultiplexed into compact tier-local storage.
+ *   [P3] vllm-project/vllm PR #42428 "W4A16 NVFP4 fused MoE", "What's in this PR":
+ *        W4A16 keeps activations in 16 bits, with no activation scales.
+ *
+ * Conventions shared by every call:
+ *   - Device pointers are allocated and owned by the caller; the library never
+ *     allocates, frees, synchronises or reads device memory back on any call that
+ *     takes a stream, so those calls can be captured into a HIP graph at fixed M.
+ *   - Every call that takes a stream enqueues its kernels on that stream and returns
+ *     before they run. A kernel fault surfaces at the caller's next synchronisation.
+ *   - Errors are status codes; moe_last_error() gives a thread-local message for the
+ *     last failing call. No C++ exception crosses this boundary.
+ *   - Layout of every weight tensor: row-major [rows, K] with K (the reduction axis)
+ *     contiguous. W13 has 2I rows, gate rows [0, I) then up rows [I, 2I), K = H.
+ *     W2 has H rows, K = I. Tier-local arrays hold that tier's experts in ascending
+ *     global id ([P2] "compact tier-local storage").
+ *   - Packed bytes: FP4 codes put element 2j in the low nibble of byte j; NF3 codes
+ *     are a little-endian bit stream per row with element j at bits [3j, 3j+3).
+ *   - Device pointers passed to moe_route, moe_align and hybrid_moe_forward must be
+ *     16-byte aligned (HMOE_ERR_ALIGN otherwise); the scratch buffer 256-byte aligned.
+ */
+#ifndef HMOE_H
+#define HMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hmoe_status {
+    HMOE_OK = 0,
+    HMOE_ERR_INVALID_ARG = 1,  /* a null, negative or inconsistent argument */
+    HMOE_ERR_UNSUPPORTED = 2,  /* a shape or option this build does not handle */
+    HMOE_ERR_ALIGN = 3,        /* a device pointer is null or misaligned */
+    HMOE_ERR_CAPACITY = 4,     /* M exceeds the layer's max_tokens */
+    HMOE_ERR_SCRATCH = 5,      /* scratch buffer smaller than moe_scratch_bytes() */
+    HMOE_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} hmoe_status;
+
+enum { HMOE_KEPT_NVFP4 = 0, HMOE_KEPT_MXFP4 = 1 };
+enum { HMOE_TIER_KEPT = 0, HMOE_TIER_NF3 = 1 };
+enum { HMOE_TENSOR_W13 = 0, HMOE_TENSOR_W2 = 1 };
+
+/* Largest M served by the decode path (M <= 8, [P1] "How it works"). */
+#define HMOE_DECODE_MAX_M 8
+
+/* Layer descriptor, read once by moe_layer_create ([P2]: tier assignment comes
+ * from the bit map; [P1]: scratch sizing from the maximum batched tokens).
+ *   num_experts  E, 1..1024
+ *   hidden       H, a multiple of 128
+ *   inter        I, a multiple of 128
+ *   top_k        k, 1..16 and <= E
+ *   max_tokens   the largest M any call will pass; sizes the scratch buffer (>= 1)
+ *   kept_format  HMOE_KEPT_NVFP4 or HMOE_KEPT_MXFP4; with a NULL bit map the layer
+ *                runs uniform NVFP4 whatever this says ([P1])
+ *   bit_map      host array of E bytes, each 4 (kept) or 3 (NF3); copied; NULL means
+ *                every expert is in the kept tier, as NVFP4
+ *   block_m      prefill rows per expert block for moe_align: 16, 32, 64 or 128; 0 picks
+ *                the library default (32) */
+typedef struct hmoe_layer_desc {
+    int32_t num_experts;
+    int32_t hidden;
+    int32_t inter;
+    int32_t top_k;
+    int32_t max_tokens;
+    int32_t kept_format;
+    const uint8_t* bit_map;
+    int32_t block_m;
+} hmoe_layer_desc;
+
+/* Opaque, immutable after creation: concurrent calls on different streams with
+ * separate scratch buffers are safe. */
+typedef struct hmoe_layer hmoe_layer;
+
+/* Host-visible facts about a created layer. */
+typedef struct hmoe_layer_info {
+    int32_t num_experts, hidden, inter, top_k, max_tokens;
+    int32_t kept_format;       /* effective format: NVFP4 when the bit map was NULL */
+    int32_t num_kept, num_nf3; /* E4 and E3 */
+    int32_t block_m;           /* effective block_m */
+    int32_t max_distinct;      /* min(8 * top_k, E): decode group capacity */
+    int32_t cap_kept, cap_nf3; /* align capacity per tier at max_tokens */
+} hmoe_layer_info;
+
+/* Packed weights of both tiers, in the layouts above. Device pointers, owned by the
+ * caller and only read. Arrays of an empty tier may be NULL.
+ *   Kept tier, NVFP4: w13_q u8 [E4, 2I, H/2], w13_s u8 [E4, 2I, H/16] (E4M3),
+ *                     w13_g f32 [E4] (per-tensor multiplier); w2_q u8 [E4, H, I/2],
+ *                     w2_s u8 [E4, H, I/16], w2_g f32 [E4].
+ *   Kept tier, MXFP4: as NVFP4 with scales u8 [.., K/32] (E8M0); the _g arrays are
+ *                     not read and may be NULL.
+ *   NF3 tier:         w13_q u8 [E3, 2I, 3H/8], w13_s u16 [E3, 2I, H/64] (fp16 bits);
+ *                     w2_q u8 [E3, H, 3I/8], w2_s u16 [E3, H, I/64]. */
+typedef struct hmoe_weights {
+    const uint8_t* kept_w13_q;
+    const uint8_t* kept_w13_s;
+    const float* kept_w13_g;
+    const uint8_t* kept_w2_q;
+    const uint8_t* kept_w2_s;
+    const float* kept_w2_g;
+    const uint8_t* nf3_w13_q;
+    const uint16_t* nf3_w13_s;
+    const uint8_t* nf3_w2_q;
+    const uint16_t* nf3_w2_s;
+} hmoe_weights;
+
+/* Device pointers into a scratch buffer: the align result of one tier, valid after
+ * moe_align or a prefill hybrid_moe_forward (M > 8) has run on that scratch.
+ *   sorted_slots  int32 [capacity]: slots s = t * k + j of the tier's experts, grouped by
+ *                 tier-local expert in ascending local id, ascending s inside an expert,
+ *                 each expert's run padded to a multiple of block_m with the sentinel M*k;
+ *                 only the first *num_padded entries are defined
+ *   block_expert  int32 [capacity / block_m]: tier-local expert of each block of block_m
+ *                 entries; only the first *num_padded / block_m entries are defined
+ *   expert_off    int32 [E_tier + 1]: exclusive prefix of the padded run lengths
+ *   num_padded    int32 [1] */
+typedef struct hmoe_align_view {
+    int32_t* sorted_slots;
+    int32_t* block_expert;
+    int32_t* expert_off;
+    int32_t* num_padded;
+    int32_t capacity;
+    int32_t num_experts_tier;
+} hmoe_align_view;
+
+/* Device pointers into a scratch buffer: the decode grouping ([P1] "M <= 8 ...
+ * direct-topk path"), valid after a decode hybrid_moe_forward (M <= 8).
+ *   counts      int32 [2]: number of distinct touched experts, and how many of them are
+ *               in the kept tier
+ *   experts     int32 [max_distinct]: distinct touched global expert ids ordered by
+ *               (tier, tier-local id); first counts[0] entries defined
+ *   num_slots   int32 [max_distinct]: number of slots routed to each
+ *   slots       int32 [max_distinct, 8]: those slots, ascending
+ *   expert_tier int32 [E]: (tier << 16) | tier-local id of every expert */
+typedef struct hmoe_decode_view {
+    int32_t* counts;
+    int32_t* experts;
+    int32_t* num_slots;
+    int32_t* slots;
+    int32_t* expert_tier;
+    int32_t max_distinct;
+} hmoe_decode_view;
+
+/* Creates a layer from a descriptor (host only; no device call). *out receives a
+ * handle owned by the library until moe_layer_destroy.
+ * Errors: HMOE_ERR_INVALID_ARG (null pointers, E < 1, k < 1, k > E, max_tokens < 1,
+ * a bit map value other than 3 or 4, an unknown kept format or block_m);
+ * HMOE_ERR_UNSUPPORTED (E > 1024, k > 16, H or I not a multiple of 128, or a K for
+ * which no decode tiling exists). */
+hmoe_status moe_layer_create(const hmoe_layer_desc* desc, hmoe_layer** out);
+
+/* Frees the handle's host memory. NULL is a no-op. */
+void moe_layer_destroy(hmoe_layer* layer);
+
+hmoe_status moe_layer_query(const hmoe_layer* layer, hmoe_layer_info* out);
+
+/* Scratch planner ([P1] "scratch sizing from max_num_batched_tokens"): bytes of
+ * device scratch that moe_align and hybrid_moe_forward need for any M <= the layer's
+ * max_tokens. Pure host arithmetic. Covers: top-k ids and weights, the expert tier
+ * map, the decode groups and decode intermediates (h and per-slot outputs for 8 * k
+ * slots, fp32), per-tier align arrays at their capacity, and, when max_tokens > 8,
+ * the prefill intermediate h [sum of capacities, I] (fp16) and the per-slot prefill
+ * outputs [max_tokens * k, H] (fp32); each region is 256-byte aligned. The caller
+ * allocates the buffer and passes it to every call. */
+hmoe_status moe_scratch_bytes(const hmoe_layer* layer, size_t* bytes);
+
+/* Softmax top-k routing, renormalised. logits: fp32 [M, E] (device). For each token,
+ * experts are ranked by logit, descending, ties to the lower expert id; topk_ids
+ * int32 [M, k] receives them in that order and topk_w fp32 [M, k] the softmax over
+ * the selected logits (= full softmax, top-k, renormalise). M = 0 is a no-op.
+ * Errors: HMOE_ERR_INVALID_ARG (M < 0, E outside 1..1024, k outside 1..min(16, E));
+ * HMOE_ERR_ALIGN; HMOE_ERR_HIP. */
+hmoe_status moe_route(const float* logits, int32_t M, int32_t E, int32_t k,
+                      int32_t* topk_ids, float* topk_w, hipStream_t stream);
+
+/* Per-tier align for the prefill path: from topk_ids int32 [M, k] (device, values in
+ * [0, E)), writes both tiers' align arrays (see hmoe_align_view) and the tier map
+ * into scratch. Deterministic; the grid is sized from max_tokens, not from data.
+ * Errors: HMOE_ERR_INVALID_ARG, HMOE_ERR_CAPACITY (M > max_tokens), HMOE_ERR_SCRATCH,
+ * HMOE_ERR_ALIGN, HMOE_ERR_HIP. */
+hmoe_status moe_align(const hmoe_layer* layer, const int32_t* topk_ids, int32_t M,
+                      void* scratch, size_t scratch_bytes, hipStream_t stream);
+
+/* Pointers to one tier's align arrays inside scratch (host arithmetic only). */
+hmoe_status moe_align_view(const hmoe_layer* layer, void* scratch, int32_t tier,
+                           hmoe_align_view* out);
+
+/* Pointers to the decode grouping inside scratch (host arithmetic only). */
+hmoe_status moe_decode_view(const hmoe_layer* layer, void* scratch, hmoe_decode_view* out);
+
+/* Pointers to the top-k ids (int32 [max_tokens, k]) and weights (fp32) that
+ * hybrid_moe_forward leaves in scratch (host arithmetic only). */
+hmoe_status moe_topk_view(const hmoe_layer* layer, void* scratch, int32_t** topk_ids,
+                          float** topk_w);
+
+/* The layer forward ([P1] "How it works", [P2] "Summary"): y = sum over each token's
+ * top-k experts of w[t, j] * SwiGLU_expert(x[t]), both tiers sharing one routing result
+ * and one sum. x: bf16 bits [M, H]; router_logits: fp32 [M, E]; y: bf16 bits [M, H],
+ * fully overwritten. M <= 8 takes the decode path (route + grouping, W13 + SwiGLU, W2 +
+ * weighted combine); M > 8 the prefill path (route, per-tier align, grouped GEMM W13 +
+ * SwiGLU, grouped GEMM W2 + weighted combine). M = 0 is a no-op returning HMOE_OK.
+ * Never allocates, synchronises or reads back: capturable in a HIP graph at fixed M.
+ * Errors: HMOE_ERR_INVALID_ARG (null layer/weights, M < 0, a needed weight array NULL),
+ * HMOE_ERR_CAPACITY, HMOE_ERR_SCRATCH, HMOE_ERR_ALIGN, HMOE_ERR_HIP. */
+hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weights,
+                               const uint16_t* x, const float* router_logits, int32_t M,
+                               uint16_t* y, void* scratch, size_t scratch_bytes,
+                               hipStream_t stream);
+
+/* Test hook: dequantises one whole expert tensor (W13: [2I, H] or W2: [H, I]) of global
+ * expert `expert` with the same device decode routines the forward kernels use, and
+ * writes the canonical values: out_f32 fp32 [rows, K] and/or out_bf16 bf16 bits
+ * [rows, K] (either may be NULL). Canonical values: NVFP4 fp32(e2m1 * e4m3) * g (one
+ * rounding), MXFP4 e2m1 * 2^(b - 127) (exact), NF3 level[q] * fp16 scale (one
+ * rounding); the bf16 form is the fp32 value rounded to nearest even.
+ * Errors: HMOE_ERR_INVALID_ARG (expert or tensor out of range, both outputs NULL, the
+ * tier's arrays NULL), HMOE_ERR_HIP. */
+hmoe_status moe_dequant(const hmoe_layer* layer, const hmoe_weights* weights,
+                        int32_t expert, int32_t tensor, float* out_f32, uint16_t* out_bf16,
+                        hipStream_t stream);
+
+/* Static string naming a status code. */
+const char* moe_status_string(hmoe_status status);
+
+/* Thread-local message describing the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HMOE_H */

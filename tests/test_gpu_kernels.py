@@ -1,0 +1,173 @@
+"""GPU parity of the integer/byte work and the dequantisation, bit for bit:
+the dequant hook against the oracle's canonical fp32 / bf16 values (edge codes
+included), routing ids (weights to 1e-6 relative), the decode grouping and the
+per-tier align tables."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import formats as F
+from oracle import layer as OL
+from hmoe_testlib import (check_output, make_layer, run_forward, scratch_for, tiny_packed,
+                          to_dev, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import weight_only_quantized_moe_amd as m
+    m.load_library()
+    return m
+
+
+# ---------------------------------------------------------------- dequant
+
+def _edge_layer(kept_format):
+    """A 2-expert layer (expert 0 kept, expert 1 NF3) whose bytes sweep the edge
+    codes: every FP4 code with every non-NaN E4M3 (or E8M0) scale byte, NVFP4
+    per-tensor scales that force rounding, NF3 fp16 scales from subnormal to max,
+    zero and negative."""
+    E, H, I, k = 2, 256, 128, 1
+    bm = np.array([4, 3], np.uint8)
+    lay = synth.empty_packed_layer(E, H, I, k, kept_format, bm)
+    r = np.random.default_rng(99)
+    kq = lay["kept"]
+    kq["w13_q"][:] = r.integers(0, 256, kq["w13_q"].shape, dtype=np.uint8)
+    kq["w2_q"][:] = r.integers(0, 256, kq["w2_q"].shape, dtype=np.uint8)
+    kq["w13_q"][0, 0, :] = np.arange(128, dtype=np.uint8)          # all code pairs
+    kq["w13_q"][0, 1, :] = np.arange(128, 256, dtype=np.uint8)
+    if kept_format == "nvfp4":
+        scales = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], np.uint8)
+        flat = kq["w13_s"].reshape(-1)
+        flat[:] = np.resize(scales, flat.size)
+        kq["w2_s"].reshape(-1)[:] = np.resize(scales[::-1], kq["w2_s"].size)
+        kq["w13_g"][:] = np.float32(1.0 / 3.0)
+        kq["w2_g"][:] = np.float32(3.0e-5)
+    else:
+        scales = np.arange(255, dtype=np.uint8)                      # 0 .. 254 (255 is NaN)
+        kq["w13_s"].reshape(-1)[:] = np.resize(scales, kq["w13_s"].size)
+        kq["w2_s"].reshape(-1)[:] = np.resize(scales[::-1], kq["w2_s"].size)
+    nq = lay["nf3"]
+    nq["w13_q"][:] = r.integers(0, 256, nq["w13_q"].shape, dtype=np.uint8)
+    nq["w2_q"][:] = r.integers(0, 256, nq["w2_q"].shape, dtype=np.uint8)
+    fp16_edges = np.array([0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001, 0xBC00,
+                           0x2E66, 0x1234], np.uint16)
+    nq["w13_s"].reshape(-1)[:] = np.resize(fp16_edges, nq["w13_s"].size)
+    nq["w2_s"].reshape(-1)[:] = np.resize(fp16_edges[::-1], nq["w2_s"].size)
+    return lay
+
+
+@pytest.mark.parametrize("case", ["tiny_nvfp4", "tiny_mxfp4", "tiny_uniform", "edge_nvfp4", "edge_mxfp4"])
+def test_dequant_bit_exact(hm, case):
+    torch = torch_mod()
+    if case.startswith("tiny"):
+        fmt = "mxfp4" if case.endswith("mxfp4") else "nvfp4"
+        packed, _ = tiny_packed(fmt, None if case.endswith("uniform") else "prefix")
+    else:
+        packed = _edge_layer(case.split("_")[1])
+    layer = make_layer(packed, 4)
+    wts = hm.DeviceWeights(packed)
+    for e in range(packed["E"]):
+        w13, w2 = OL.expert_weights(packed, e)
+        for tensor, ref in ((hm.TENSOR_W13, w13), (hm.TENSOR_W2, w2)):
+            out = torch.empty(ref.shape, dtype=torch.float32, device="cuda")
+            outb = torch.empty(ref.shape, dtype=torch.int16, device="cuda")
+            hm.moe_dequant(layer, wts, e, tensor, out, outb)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), \
+                f"{case} expert {e} tensor {tensor}: " \
+                f"{np.sum(got.view(np.uint32) != ref.view(np.uint32))} fp32 mismatches"
+            gotb = outb.cpu().numpy().view(np.uint16)
+            assert np.array_equal(gotb, F.bf16_bits(ref)), f"{case} expert {e} tensor {tensor}: bf16"
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("M,E,k,kind", [
+    (1, 8, 2, "normal"), (7, 128, 8, "normal"), (64, 256, 8, "normal"), (1000, 1000, 16, "normal"),
+    (300, 256, 8, "ties"), (33, 64, 64 // 4, "ties"), (5, 3, 3, "normal"), (20, 256, 1, "zeros"),
+])
+def test_route_matches_oracle(hm, M, E, k, kind):
+    torch = torch_mod()
+    r = np.random.default_rng(M * 1000 + E)
+    if kind == "normal":
+        lg = r.standard_normal((M, E)).astype(np.float32)
+    elif kind == "ties":
+        lg = r.integers(-2, 3, (M, E)).astype(np.float32)
+        lg[:, ::3] *= -1.0   # introduces -0.0 next to +0.0
+    else:
+        lg = np.zeros((M, E), np.float32)
+        lg[:, 1::2] = -0.0
+    ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, k), dtype=torch.float32, device="cuda")
+    hm.moe_route(to_dev(lg), k, ids, w)
+    torch.cuda.synchronize()
+    ref_ids, ref_w = OL.route(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    rel = np.abs(w.cpu().numpy().astype(np.float64) - ref_w) / ref_w
+    assert rel.max() <= 1e-6, rel.max()
+
+
+# ---------------------------------------------------------------- decode grouping
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_decode_grouping_bit_exact(hm, M):
+    torch = torch_mod()
+    w = synth.qwen_decode(M)
+    packed = synth.packed_layer(w)
+    layer = make_layer(packed, 8)
+    wts = hm.DeviceWeights(packed)
+    x = synth.activations_bf16(w, M)
+    lg = synth.router_logits(w, M)
+    _, scratch = run_forward(layer, wts, x, lg)
+    v = hm.moe_decode_view(layer, scratch)
+    tier, local = OL.tier_map(packed["bit_map"], w.E)
+    ids, _ = OL.route(lg, w.top_k)
+    groups = OL.decode_groups(ids, tier, local)
+    counts = v["counts"].cpu().numpy()
+    assert counts[0] == len(groups) and counts[1] == sum(1 for g in groups if g[1] == 0)
+    experts = v["experts"].cpu().numpy()[: len(groups)]
+    nslots = v["num_slots"].cpu().numpy()
+    slots = v["slots"].cpu().numpy()
+    for d, (e, t, l, sl) in enumerate(groups):
+        assert experts[d] == e and nslots[d] == len(sl) and list(slots[d, : len(sl)]) == sl
+    et = v["expert_tier"].cpu().numpy()
+    assert np.array_equal(et >> 16, tier) and np.array_equal(et & 0xFFFF, local)
+    tids, tw = hm.moe_topk_view(layer, scratch, M)
+    assert np.array_equal(tids.cpu().numpy(), ids)
+
+
+# ---------------------------------------------------------------- align
+
+@pytest.mark.parametrize("E,k,M,bm,n_kept", [
+    (8, 2, 9, 16, 4), (8, 2, 100, 32, 4), (256, 8, 64, 32, 64), (256, 8, 4096, 32, 64),
+    (256, 8, 512, 128, 64), (128, 8, 300, 64, 32), (256, 8, 700, 16, None), (64, 4, 1, 64, 16),
+])
+def test_align_bit_exact(hm, E, k, M, bm, n_kept):
+    torch = torch_mod()
+    r = np.random.default_rng(E + M + bm)
+    bit_map = None
+    if n_kept is not None:
+        bit_map = np.full(E, 3, np.uint8)
+        bit_map[r.permutation(E)[:n_kept]] = 4
+    lg = (r.standard_normal((M, E)) + 1.5 * r.standard_normal(E)[None, :]).astype(np.float32)
+    ids, _ = OL.route(lg, k)
+    layer = hm.moe_layer_create(E, 256, 128, k, M, hm.KEPT_NVFP4, bit_map, bm)
+    scratch = scratch_for(layer)
+    scratch.fill_(0xAB)     # stale contents must not leak into the defined entries
+    hm.moe_align(layer, to_dev(ids), M, scratch)
+    torch.cuda.synchronize()
+    tier, local = OL.tier_map(bit_map, E)
+    ref = OL.align(ids, tier, local, bm)
+    for t in (0, 1):
+        v = hm.moe_align_view(layer, scratch, t)
+        npad = int(v["num_padded"].cpu().numpy()[0])
+        assert npad == ref[t]["num_padded"]
+        assert np.array_equal(v["sorted_slots"].cpu().numpy()[:npad], ref[t]["sorted_slots"])
+        assert np.array_equal(v["block_expert"].cpu().numpy()[: npad // bm], ref[t]["block_expert"])
+        assert np.array_equal(v["expert_off"].cpu().numpy(), ref[t]["expert_off"])

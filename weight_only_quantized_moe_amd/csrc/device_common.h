@@ -1,0 +1,151 @@
+// Device primitives shared by the hybrid W4A16 MoE kernels (gfx950 only).
+//
+// Formats (named by the hybrid NVFP4/NF3 serving pages, local-inference-lab/vllm
+// PR #92 "How it works" and PR #104 description; bit layouts from the OCP MX v1.0
+// and OCP OFP8 specifications):
+//   E2M1  4-bit element: sign, 2 exponent bits (bias 1), 1 mantissa bit.
+//   E4M3  8-bit NVFP4 block scale ("fn": no infinities, 0x7F/0xFF NaN).
+//   E8M0  8-bit MXFP4 block scale: 2^(b - 127).
+//   NF3   3-bit NormalFloat level index with an fp16 group scale.
+// gfx950 decodes E2M1 and E4M3 in hardware (v_cvt_scalef32_pk_*_fp4 with a scale
+// whose exponent only is applied, and v_cvt_f32_fp8 for OCP E4M3); NF3 goes through
+// an LDS-resident table of level pairs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hmoe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// NF3 levels: the 3-bit NormalFloat code book (QLoRA's NormalFloat construction
+// carried out at 3 bits: 4 positive and 3 negative standard-normal quantiles plus
+// an exact zero, scaled so that the ends are -1 and +1), as fp32 bit patterns in
+// ascending level order.
+// ---------------------------------------------------------------------------
+__device__ __constant__ static const uint32_t kNF3Bits[8] = {
+    0xBF800000u, 0xBF08F740u, 0xBE7CDB98u, 0x00000000u,
+    0x3E3BBCD2u, 0x3EC394B6u, 0x3F1F7BFEu, 0x3F800000u};
+
+__device__ __forceinline__ float nf3_level(uint32_t q) { return __uint_as_float(kNF3Bits[q & 7]); }
+
+// Level tables inside the kernels hold level * c rounded to 16 bits, with c chosen
+// so that all eight products are close to representable: the largest relative
+// rounding error is 5.5e-4 in bf16 (c = 1.2417735) and 3.5e-5 in fp16 (c =
+// 1.1152737), against 3.0e-3 and 2.5e-4 for the plain levels. The kernels take
+// the group scale in fp32 and multiply each row result by 1/c.
+constexpr float kNF3TableScaleBf16 = 1.2417735f;
+constexpr float kNF3TableScaleF16 = 1.1152737f;
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// two fp32 -> packed bf16 pair, round to nearest even (a in the low half)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 f = {a, b};
+  const bf16x2 v = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32 (RNE)
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// two fp32 -> packed fp16 pair, round to nearest even (a in the low half)
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  const f32x2 f = {a, b};
+  const f16x2 v = __builtin_convertvector(f, f16x2);  // v_cvt_pk_f16_f32 (RNE)
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp16 bits -> fp32 (exact)
+__device__ __forceinline__ float fp16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// E4M3 byte `sel` of v -> fp32 (exact, hardware decode of OCP E4M3)
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t v) { return __builtin_amdgcn_cvt_f32_fp8(v, SEL); }
+
+// E8M0 byte -> the fp32 whose exponent field encodes 2^(b - 127); used as the scale
+// operand of the scaled FP4 conversions, which apply only that exponent. Byte 0 is
+// given a nonzero mantissa so the operand is the fp32 subnormal 2^-127 itself.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t b) {
+  return __uint_as_float((b << 23) | (b == 0 ? 0x00400000u : 0u));
+}
+
+// exact fp32 value 2^(b - 127) of an E8M0 byte
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return __uint_as_float(b == 0 ? 0x00400000u : (b << 23));
+}
+
+// E2M1 pair in byte SEL of v -> two bf16 (low nibble -> low half) times 2^exp(scale)
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_bf16(uint32_t v, float scale) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// E2M1 pair in byte SEL of v -> two fp32 times 2^exp(scale) (exact)
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_f32(uint32_t v, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, scale, SEL);
+}
+
+// E2M1 pair in byte SEL of v -> two fp16 (low nibble -> low half) times 2^exp(scale)
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_f16(uint32_t v, float scale) {
+  f16x2 r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, scale, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// dot of two fp16 pairs accumulated in fp32
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                false);
+}
+
+// dot of two bf16 pairs accumulated in fp32
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// 6-bit NF3 pair field p (elements 2p, 2p+1) of a 32-element unit stored as three
+// little-endian dwords (element j at bits [3j, 3j+3) of the 96-bit unit)
+template <int P>
+__device__ __forceinline__ uint32_t nf3_pair_field(uint32_t d0, uint32_t d1, uint32_t d2) {
+  constexpr int bit = 6 * P;
+  if constexpr (bit + 6 <= 32) {
+    return __builtin_amdgcn_ubfe(d0, bit, 6);
+  } else if constexpr (bit < 32) {
+    return __builtin_amdgcn_alignbit(d1, d0, bit) & 63u;
+  } else if constexpr (bit + 6 <= 64) {
+    return __builtin_amdgcn_ubfe(d1, bit - 32, 6);
+  } else if constexpr (bit < 64) {
+    return __builtin_amdgcn_alignbit(d2, d1, bit - 32) & 63u;
+  } else {
+    return __builtin_amdgcn_ubfe(d2, bit - 64, 6);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions (64 lanes); WIDTH-lane groups must be aligned powers of two
+// ---------------------------------------------------------------------------
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, WIDTH);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace hmoe

@@ -1,0 +1,81 @@
+// Internal declarations of libhmoe: the layer object, the scratch plan and the
+// kernel launchers each kernel file provides. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/hmoe.h"
+
+namespace hmoe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kDecodeMaxM = HMOE_DECODE_MAX_M;
+
+// Byte offsets of every scratch region (each 256-byte aligned).
+struct ScratchPlan {
+  size_t topk_ids = 0, topk_w = 0, expert_tier = 0;
+  size_t d_counts = 0, d_experts = 0, d_nslots = 0, d_slots = 0;
+  size_t h_dec = 0, o_dec = 0;
+  size_t a_counts = 0;                     // int32 [E] slot counts per expert
+  size_t a_slots[2] = {0, 0}, a_bexp[2] = {0, 0}, a_eoff[2] = {0, 0}, a_npad[2] = {0, 0};
+  size_t h_pre = 0, o_pre = 0;
+  size_t total = 0;
+};
+
+// GEMV tiling of one weight tensor on the decode path: lanes per row (LR), units of
+// 32 K-elements per lane (KU), rows per task.
+struct GemvTiling {
+  int lr = 0, ku = 0, rows_per_task = 0;
+};
+
+struct Layer {
+  int E = 0, H = 0, I = 0, k = 0, max_tokens = 0;
+  int kept_format = HMOE_KEPT_NVFP4;  // effective
+  int block_m = 32;
+  bool has_map = false;
+  std::vector<uint8_t> bit_map;
+  int E4 = 0, E3 = 0;
+  uint32_t nf3_mask[kMaxExperts / 32] = {};  // bit e set: expert e is in the NF3 tier
+  int max_distinct = 0;                        // min(8k, E)
+  int cap[2] = {0, 0};                         // align capacity per tier
+  GemvTiling w13, w2;
+  ScratchPlan plan;
+};
+
+// Expert-tier bit mask passed by value to the kernels that need the tier map.
+struct TierMask {
+  uint32_t w[kMaxExperts / 32];
+};
+
+// ---- launchers (each returns hipGetLastError() of its launch) -------------------
+
+// route.hip
+hipError_t launch_route(const float* logits, int M, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s);
+hipError_t launch_route_group(const Layer& L, const float* logits, int M, void* scratch,
+                              hipStream_t s);
+
+// align.hip
+hipError_t launch_align(const Layer& L, const int32_t* ids, int M, void* scratch, hipStream_t s);
+
+// decode.hip
+hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
+                         uint16_t* y, void* scratch, hipStream_t s);
+
+// prefill.hip
+hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
+                          uint16_t* y, void* scratch, hipStream_t s);
+
+// dequant.hip
+hipError_t launch_dequant(const Layer& L, const hmoe_weights& W, int expert, int tensor,
+                          float* out_f32, uint16_t* out_bf16, hipStream_t s);
+
+TierMask make_tier_mask(const Layer& L);
+
+}  // namespace hmoe
