@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid W4A16 MoE layer (NVFP4/MXFP4 kept tier + NF3 tail) on
+one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload: the Qwen3-MoE-shaped decode layer (E=128, H=2048, I=768, top-8,
+32 NVFP4 + 96 NF3 experts), M = 8 tokens per step, with the M = 1, 2, 4 points of
+the decode sweep reported beside it. Other workloads (--workload): glm_decode
+(E=256, H=6144, I=2048, M=8), glm_prefill (M=4096, skewed routing), glm_mxfp4
+(MXFP4 kept tier, M=512) and glm_uniform (no bit map, uniform NVFP4, M=512).
+
+One step is one hybrid_moe_forward over one batch: routing, grouping or align,
+both tiers' W13 + SwiGLU, W2 + weighted combine. Steps replay HIP graphs of the
+forward that rotate over enough copies of the packed weights to exceed the
+256 MB Infinity Cache, so every step reads its experts from HBM. Inputs are
+synthetic (seeded), resident in HBM before timing starts.
+
+Prints one JSON line. `roofline` covers the dominant kernel (decode: the W13
+GEMV; prefill: the W13 grouped GEMM), timed live with HIP events on the launch
+stream; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode tok/s + HBM GB/s (M<=8); prefill TFLOP/s (M=4096)"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 * 1024 * 1024
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def workload(name, m):
+    import synth
+    table = {"qwen_decode": synth.qwen_decode, "glm_decode": synth.glm_decode,
+             "glm_prefill": synth.glm_prefill, "glm_mxfp4": synth.glm_mxfp4,
+             "glm_uniform": synth.glm_uniform}
+    fn = table[name]
+    return fn() if m is None else fn(m)
+
+
+def describe(w, packed):
+    bm = packed["bit_map"]
+    n_kept = w.E if bm is None else int((bm == 4).sum())
+    kept = packed["kept_format"].upper()
+    tiers = f"{n_kept} {kept} + {w.E - n_kept} NF3" if bm is not None else f"uniform {kept}"
+    return f"{w.name}: E={w.E} H={w.H} I={w.I} top-{w.top_k} SwiGLU, {tiers}"
+
+
+def expert_bytes(packed):
+    """Packed bytes of one expert's W13 and W2 per tier: codes + scales + global."""
+    out = {}
+    for tier in ("kept", "nf3"):
+        d = packed[tier]
+        if d["w13_q"].shape[0] == 0:
+            continue
+        per = lambda key: d[key][0].nbytes if key in d else 0
+        g = 4 if (tier == "kept" and packed["kept_format"] == "nvfp4") else 0
+        out[tier] = {"w13": per("w13_q") + per("w13_s") + g, "w2": per("w2_q") + per("w2_s") + g}
+    return out
+
+
+def source_hash(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "weight_only_quantized_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(kernel_key, src_hash, launches_bytes):
+    """HBM traffic per launch of the dominant kernel from committed rocprofv3 --pmc
+    counts (profiles/pmc_traffic.json), or None if they were taken on other source."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        rec = data.get(kernel_key)
+        if not rec or rec.get("source_hash") != src_hash:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None):
+    """Times `steps` graph replays of the forward at w.M; returns a result dict."""
+    import numpy as np
+    import torch
+
+    import synth
+    import weight_only_quantized_moe_amd as hm
+
+    if packed is None:
+        t0 = time.time()
+        packed = synth.packed_layer(w)
+        log(f"{w.name}: generated packed layer in {time.time() - t0:.1f}s")
+    bm = packed["bit_map"]
+    fmt = hm.KEPT_NVFP4 if packed["kept_format"] == "nvfp4" else hm.KEPT_MXFP4
+    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, 32)
+    base = hm.DeviceWeights(packed)
+    layer_bytes = base.nbytes()
+    if copies is None:
+        copies = max(1, math.ceil(4 * MALL_BYTES / layer_bytes))
+    wts = [base] + [base.clone() for _ in range(copies - 1)]
+    scratch = torch.zeros(hm.moe_scratch_bytes(layer), dtype=torch.uint8, device="cuda")
+    x = torch.from_numpy(synth.activations_bf16(w, w.M).view(np.int16)).cuda()
+    lg = torch.from_numpy(synth.router_logits(w, w.M)).cuda()
+    y = torch.empty((w.M, w.H), dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+
+    # eager warm-up (also fills the decode view / align tables for the byte counts)
+    for i in range(3):
+        hm.hybrid_moe_forward(layer, wts[i % copies], x, lg, y, scratch)
+    torch.cuda.synchronize()
+
+    # one HIP graph per weight copy
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                hm.hybrid_moe_forward(layer, wts[c], x, lg, y, scratch)
+            graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / steps
+
+    # per-stage durations, live, with HIP events on the launch stream; a GPU sleep
+    # first lets the host queue every launch so the kernels run back to back
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(stage_steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))
+    for i in range(stage_steps):
+        wt = wts[i % copies]
+        ev[i][0].record()
+        for st in range(4):
+            hm.hybrid_moe_forward_stage(layer, wt, x, lg, y, scratch, st)
+            ev[i][st + 1].record()
+    torch.cuda.synchronize()
+    stage_us = [sum(ev[i][st].elapsed_time(ev[i][st + 1]) for i in range(stage_steps)) * 1e3 / stage_steps
+                for st in range(4)]
+
+    # algorithmic work from the routing this batch produced
+    eb = expert_bytes(packed)
+    k, M = w.top_k, w.M
+    res = {"ms_per_step": ms_per_step, "stage_us": stage_us, "copies": copies,
+           "layer_bytes_resident": layer_bytes, "desc": describe(w, packed)}
+    io_bytes = M * w.H * 2 + M * w.E * 4 + M * w.H * 2        # x, logits, y
+    if M <= hm.DECODE_MAX_M:
+        v = hm.moe_decode_view(layer, scratch)
+        counts = v["counts"].cpu().numpy()
+        nd, nk = int(counts[0]), int(counts[1])
+        n_tier = {"kept": nk, "nf3": nd - nk}
+        w13 = sum(n_tier[t] * eb[t]["w13"] for t in eb)
+        w2 = sum(n_tier[t] * eb[t]["w2"] for t in eb)
+        res.update(distinct_experts=nd, distinct_kept=nk,
+                   layer_bytes=w13 + w2 + io_bytes,
+                   w13_bytes=w13 + M * w.H * 2 + M * k * w.I * 2)
+    else:
+        touched = {}
+        for t, name in ((0, "kept"), (1, "nf3")):
+            if name not in eb:
+                continue
+            off = hm.moe_align_view(layer, scratch, t)["expert_off"].cpu().numpy()
+            touched[name] = int((np.diff(off) > 0).sum())
+        wbytes = sum(touched[t] * (eb[t]["w13"] + eb[t]["w2"]) for t in touched)
+        res.update(touched_experts=touched, layer_bytes=wbytes + io_bytes,
+                   flops=6.0 * M * k * w.H * w.I, w13_flops=4.0 * M * k * w.H * w.I)
+    res["packed"] = packed
+    res["inputs"] = (synth.activations_bf16(w, w.M), synth.router_logits(w, w.M))
+    del graphs, wts, base
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(packed, x_bits, logits, budget_s=15.0, tokens=None):
+    """The oracle as it stands, on the same layer and batch (or on a sample of its
+    tokens, routed with the whole batch), repeated until about budget_s seconds of
+    CPU work."""
+    from oracle import layer as OL
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        pass
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        OL.forward(packed, x_bits, logits, tokens=tokens)
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s or runs >= 20:
+            break
+    el = time.perf_counter() - t0
+    M = x_bits.shape[0]
+    n = M if tokens is None else len(tokens)
+    what = f"the M={M} batch" if tokens is None else f"{n} of the M={M} tokens (routing all {M})"
+    return {"value": n * runs / el, "unit": "tok/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "runs": runs, "seconds": el,
+            "sample": f"{runs} oracle forwards of {what}: route, fp32 dequant of the touched "
+                      f"experts, fp64 SwiGLU MLPs, combine; numpy, BLAS threads as `cores`, "
+                      f"elementwise work single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="qwen_decode",
+                    choices=["qwen_decode", "glm_decode", "glm_prefill", "glm_mxfp4", "glm_uniform"])
+    ap.add_argument("--m", type=int, default=None, help="override the batch size")
+    ap.add_argument("--copies", type=int, default=None, help="weight copies to rotate")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the M=1,2,4 decode sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the hybrid MoE layer "
+                                   "is measured on one MI355X with the full layer resident; "
+                                   "multi-GPU sharding is not implemented (see DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    import weight_only_quantized_moe_amd as hm
+    hm.load_library()
+
+    w = workload(args.workload, args.m)
+    decode = w.M <= hm.DECODE_MAX_M
+    log(f"measuring {w.name} (M={w.M}), {args.steps} steps after {args.warmup} warm-up")
+    r = measure(w, args.steps, args.warmup, args.copies)
+    ms = r["ms_per_step"]
+    out = {
+        "metric": METRIC,
+        "value": w.M / (ms * 1e-3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": r["desc"], "M": w.M, "tokens_per_step": w.M,
+                   "weight_copies_rotated": r["copies"], "launch": "hip_graph_replay",
+                   "parallelism": "single_gpu"},
+        "hbm_gbps": r["layer_bytes"] / (ms * 1e-3) / 1e9,
+        "layer_bytes_per_step": r["layer_bytes"],
+        "stage_us": dict(zip(["route", "w13", "w2", "combine"], [round(v, 2) for v in r["stage_us"]])),
+    }
+    src = source_hash("decode.hip" if decode else "prefill.hip", "device_common.h")
+    if decode:
+        t_w13 = r["stage_us"][1] * 1e-6
+        achieved = r["w13_bytes"] / t_w13 / 1e9
+        out["distinct_experts"] = r["distinct_experts"]
+        out["roofline"] = {"bound": "hbm", "kernel": "gemv_kernel<W13> (decode W13 + SwiGLU)",
+                           "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": achieved / HBM_PEAK_GBPS, "algorithmic_bytes": r["w13_bytes"],
+                           "avg_launch_us": r["stage_us"][1],
+                           "traffic": pmc_traffic("decode_w13_" + w.name, src, r["w13_bytes"])}
+        out["config"]["distinct_experts"] = r["distinct_experts"]
+    else:
+        t_w13 = r["stage_us"][1] * 1e-6
+        achieved = r["w13_flops"] / t_w13 / 1e12
+        out["tflops"] = r["flops"] / (ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "grouped_gemm_kernel<W13> (prefill W13 + SwiGLU)",
+                           "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": r["w13_flops"],
+                           "avg_launch_us": r["stage_us"][1],
+                           "traffic": pmc_traffic("prefill_w13_" + w.name, src, None)}
+        out["config"]["touched_experts"] = r["touched_experts"]
+    if decode and args.workload == "qwen_decode" and not args.no_sweep and args.m is None:
+        sweep = []
+        for m in (1, 2, 4):
+            wm = workload(args.workload, m)
+            rm = measure(wm, args.steps, args.warmup, args.copies, packed=r["packed"])
+            sweep.append({"M": m, "tok_per_s": m / (rm["ms_per_step"] * 1e-3),
+                          "ms_per_step": rm["ms_per_step"],
+                          "hbm_gbps": rm["layer_bytes"] / (rm["ms_per_step"] * 1e-3) / 1e9,
+                          "w13_frac_of_hbm_peak": rm["w13_bytes"] / (rm["stage_us"][1] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                          "distinct_experts": rm["distinct_experts"]})
+        sweep.append({"M": w.M, "tok_per_s": out["value"], "ms_per_step": ms, "hbm_gbps": out["hbm_gbps"],
+                      "w13_frac_of_hbm_peak": out["roofline"]["frac"], "distinct_experts": r["distinct_experts"]})
+        out["sweep"] = sweep
+    if not args.no_cpu_baseline:
+        x_bits, logits = r["inputs"]
+        log("timing the CPU oracle")
+        cb = cpu_baseline(r["packed"], x_bits, logits, args.cpu_budget,
+                          tokens=None if decode else [0, 1])
+        if not decode:
+            cb["value_tflops"] = r["flops"] * cb["value"] / w.M / 1e12
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

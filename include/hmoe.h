@@ -63,6 +63,8 @@ typedef enum hmoe_status {
 enum { HMOE_KEPT_NVFP4 = 0, HMOE_KEPT_MXFP4 = 1 };
 enum { HMOE_TIER_KEPT = 0, HMOE_TIER_NF3 = 1 };
 enum { HMOE_TENSOR_W13 = 0, HMOE_TENSOR_W2 = 1 };
+/* Stages of the forward, in launch order (see hybrid_moe_forward_stage). */
+enum { HMOE_STAGE_ROUTE = 0, HMOE_STAGE_W13 = 1, HMOE_STAGE_W2 = 2, HMOE_STAGE_COMBINE = 3 };
 
 /* Largest M served by the decode path (M <= 8, [P1] "How it works"). */
 #define HMOE_DECODE_MAX_M 8
@@ -229,6 +231,20 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
                                const uint16_t* x, const float* router_logits, int32_t M,
                                uint16_t* y, void* scratch, size_t scratch_bytes,
                                hipStream_t stream);
+
+/* One stage of hybrid_moe_forward, for profiling: with the same arguments, calling
+ * HMOE_STAGE_ROUTE, _W13, _W2 and _COMBINE in that order on one stream is exactly
+ * hybrid_moe_forward. ROUTE is routing plus the decode grouping (M <= 8) or routing
+ * plus the per-tier align (M > 8); W13 is the expert up projection with the fused
+ * SwiGLU; W2 the down projection with the routing weight; COMBINE the fixed-order
+ * top-k sum into y. Each stage reads what the previous stages left in scratch, so a
+ * stage run out of order computes from stale scratch contents (no fault, since every
+ * index it reads is bounds-checked or produced by ROUTE for this layer).
+ * Errors: as hybrid_moe_forward, plus HMOE_ERR_INVALID_ARG for an unknown stage. */
+hmoe_status hybrid_moe_forward_stage(const hmoe_layer* layer, const hmoe_weights* weights,
+                                     const uint16_t* x, const float* router_logits, int32_t M,
+                                     uint16_t* y, void* scratch, size_t scratch_bytes,
+                                     int32_t stage, hipStream_t stream);
 
 /* Test hook: dequantises one whole expert tensor (W13: [2I, H] or W2: [H, I]) of global
  * expert `expert` with the same device decode routines the forward kernels use, and

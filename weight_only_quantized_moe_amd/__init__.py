@@ -21,12 +21,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhmoe.so"
 KEPT_NVFP4, KEPT_MXFP4 = 0, 1
 TIER_KEPT, TIER_NF3 = 0, 1
 TENSOR_W13, TENSOR_W2 = 0, 1
+STAGE_ROUTE, STAGE_W13, STAGE_W2, STAGE_COMBINE = 0, 1, 2, 3
 DECODE_MAX_M = 8
 
 EXPORTED = (
     "moe_layer_create", "moe_layer_destroy", "moe_layer_query", "moe_scratch_bytes",
     "moe_route", "moe_align", "moe_align_view", "moe_decode_view", "moe_topk_view",
-    "hybrid_moe_forward", "moe_dequant", "moe_status_string", "moe_last_error",
+    "hybrid_moe_forward", "hybrid_moe_forward_stage", "moe_dequant", "moe_status_string", "moe_last_error",
 )
 
 
@@ -98,6 +99,9 @@ def load_library() -> ctypes.CDLL:
     lib.hybrid_moe_forward.argtypes = [c_void_p, POINTER(Weights), c_void_p, c_void_p, c_int32,
                                        c_void_p, c_void_p, c_size_t, c_void_p]
     lib.hybrid_moe_forward.restype = st
+    lib.hybrid_moe_forward_stage.argtypes = [c_void_p, POINTER(Weights), c_void_p, c_void_p, c_int32,
+                                             c_void_p, c_void_p, c_size_t, c_int32, c_void_p]
+    lib.hybrid_moe_forward_stage.restype = st
     lib.moe_dequant.argtypes = [c_void_p, POINTER(Weights), c_int32, c_int32, c_void_p, c_void_p,
                                 c_void_p]
     lib.moe_dequant.restype = st
@@ -238,6 +242,15 @@ def hybrid_moe_forward(layer: Layer, weights: "DeviceWeights", x, router_logits,
     _check(load_library().hybrid_moe_forward(
         layer.handle, byref(weights.struct), _ptr(x), _ptr(router_logits), M, _ptr(y),
         _ptr(scratch), scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def hybrid_moe_forward_stage(layer: Layer, weights: "DeviceWeights", x, router_logits, y, scratch,
+                             stage: int, stream=None) -> None:
+    """One stage of hybrid_moe_forward (STAGE_ROUTE, _W13, _W2, _COMBINE, in order)."""
+    M = x.shape[0]
+    _check(load_library().hybrid_moe_forward_stage(
+        layer.handle, byref(weights.struct), _ptr(x), _ptr(router_logits), M, _ptr(y),
+        _ptr(scratch), scratch.numel() * scratch.element_size(), stage, _stream(stream)))
 
 
 def moe_dequant(layer: Layer, weights: "DeviceWeights", expert: int, tensor: int,

@@ -1,32 +1,40 @@
-// Decode path (M <= 8): route + grouping, then for every distinct touched expert a
-// GEMV over its packed W13 with a fused SwiGLU, a GEMV over its packed W2, and the
-// deterministic top-k weighted combine into y. Both tiers run in the same launches
-// from one routing result (local-inference-lab/vllm PR #92, "How it works": launches
-// sharing one route geometry and one top-k sum; M <= 8 addressed directly by the
-// top-k result).
+// Decode path (M <= 8): after routing and grouping, a GEMV over the packed W13 of
+// every distinct touched expert with a fused SwiGLU, a GEMV over their packed W2,
+// and the deterministic top-k weighted combine into y. Both tiers run in the same
+// launches from one routing result (local-inference-lab/vllm PR #92, "How it
+// works": launches sharing one route geometry and one top-k sum; M <= 8 addressed
+// directly by the top-k result).
 //
-// GEMV mapping: a task is (distinct expert d, tile of rows). The 4 waves of a block
-// split K into WK parts and the task's rows into 4/WK groups. Inside a wave, LR lanes
-// share a row and each lane owns KU units of 32 K-elements (unit u = c + LR*j), so a
-// wave instruction reads LR consecutive 16-byte (FP4) or 12-byte (NF3) units of P =
-// 64/LR rows. The lane keeps the matching activations of up to two tokens in
-// registers as 16-bit pairs and meets the decoded weight pairs in v_dot2_f32_*.
+// Work split: the rows of all touched experts form one flat range (W13: pairs of a
+// gate row i and its up row I + i; W2: rows n). It is cut into chunks of P * RI rows
+// (or pairs) and every wave of a persistent grid takes one contiguous, balanced run
+// of chunks, so each wave streams long stretches of one or two experts and reloads
+// its activations only when the expert changes. Inside a wave, LR lanes share a row
+// and each lane owns KU units of 32 K-elements (unit u = c + LR*j), so one load
+// instruction reads LR consecutive 16-byte (FP4) or 12-byte (NF3) units of each of
+// P = 64/LR rows. The lane's activations sit in
+// registers as 16-bit pairs and meet the decoded weights in v_dot2_f32_*; per-row
+// sums are finished by a transposing reduction across the LR lanes. A wave serves
+// one token per pass over its range; an expert with several tokens re-streams the
+// range (from cache) once per token, which keeps the activations, two chunks of
+// weights in flight, and the decoded values within the register budget.
 //
-// Precision: W13 runs on bf16 pairs (x is bf16; E2M1 values are exact in bf16; the
-// NVFP4 E4M3 block scale multiplies the fp32 partial of its 16-block; MXFP4's
-// power-of-two scale is folded into the conversion; NF3 levels come from a scaled
-// table, see kNF3TableScaleBf16, with the fp16 group scale on the fp32 partial). h
-// leaves W13 in fp32. W2 runs on fp16 pairs: each slot's h row is scaled by a power
-// of two so its largest magnitude lands in [2^14, 2^15), which keeps 11 significant
-// bits for every element that matters; E2M1 is exact in fp16 and every block or
-// group scale again multiplies an fp32 partial.
+// Precision: W13 runs on bf16 pairs (x is bf16; E2M1 is exact in bf16; the NVFP4
+// E4M3 block scale multiplies each 16-block's fp32 partial; MXFP4's power-of-two
+// scale is folded into the conversion; NF3 levels come from a scaled table, see
+// kNF3TableScaleBf16, with the fp16 group scale on the fp32 partial). h leaves W13
+// in fp32. W2 runs on fp16 pairs: each slot's h row is scaled by a power of two so
+// its largest magnitude lands in [2^14, 2^15); E2M1 is exact in fp16 and every block
+// or group scale multiplies an fp32 partial.
+#include <type_traits>
+
 #include "device_common.h"
 #include "hmoe_internal.h"
 
 namespace hmoe {
 
 constexpr int kGemvThreads = 256;
-constexpr int kMaxTaskRows = 256;
+constexpr int kGemvWaves = kGemvThreads / kWave;
 
 struct GemvArgs {
   const uint8_t* kq;   // kept codes [E4, rows, K/2]
@@ -35,21 +43,55 @@ struct GemvArgs {
   const uint8_t* nq;   // NF3 codes [E3, rows, 3K/8]
   const uint16_t* ns;  // NF3 scales [E3, rows, K/64]
   int kept_fmt;
-  int rows, K;
+  int rows, K;       // rows of the weight tensor per expert, reduction length
+  int out_units;     // W13: I (row pairs per expert); W2: H (rows per expert)
   const uint16_t* act_bf16;  // W13: x bf16 [M, K]
   const float* act_f32;      // W2: h fp32 [slots, K]
-  int act_row_div;           // activation row of slot s is s / act_row_div
+  int k;                     // top-k (x row of slot s is s / k)
   const int32_t* counts;
-  const int32_t* experts;
-  const int32_t* nslots;
-  const int32_t* slots;
-  const int32_t* expert_tier;
-  int tile_rows;  // output rows per task (W13: gate rows; each also brings its up row)
-  int tiles;      // tasks per expert
-  int I;          // W13: row offset of the up projection
-  float* h_out;   // W13: fp32 [slots, I]
-  float* o_out;   // W2: fp32 [slots, rows]
+  const int32_t* recs;   // group records [bound, kGroupRec]
+  int bound;              // distinct experts at most (min(M*k, E))
+  int E, E4, E3, nslot;   // range checks of what the grouping left in scratch
+  int I;
+  float* h_out;  // W13: fp32 [slots, I]
+  float* o_out;  // W2: fp32 [slots, H]
 };
+
+// Transposing reduction of V values per lane over aligned LR-lane segments (V <= LR,
+// both powers of two): each step keeps one half of the values and adds the partner
+// lane's other half (partners from xlane), so V sums cost V - 1 + log2(LR / V)
+// exchanges instead of V * log2(LR). The lane ends with the sum of value index
+// seg_index<V, LR>(lane).
+template <int V, int LR>
+__device__ __forceinline__ float seg_reduce(const float (&v)[V]) {
+  if constexpr (V == 1) {
+    return group_sum<LR>(v[0]);
+  } else {
+    constexpr int H = V / 2;
+    constexpr int off = LR / 2;
+    const bool hi = (threadIdx.x & off) != 0;
+    float nv[H];
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const float keep = hi ? v[j + H] : v[j];
+      const float send = hi ? v[j] : v[j + H];
+      nv[j] = keep + xlane<off>(send);
+    }
+    return seg_reduce<H, LR / 2>(nv);
+  }
+}
+
+template <int V, int LR>
+__device__ __forceinline__ int seg_index(int lane) {
+  int o = 0;
+#pragma unroll
+  for (int v = V, lr = LR; v > 1;) {
+    lr >>= 1;
+    v >>= 1;
+    if (lane & lr) o += v;
+  }
+  return o;
+}
 
 // Partial dot products of one lane for one row over its KU units. F16 selects the
 // fp16 pair path (W2) over the bf16 one (W13).
@@ -71,18 +113,14 @@ struct RowDot {
     w[12] = fp4<0>(q.w, s); w[13] = fp4<1>(q.w, s); w[14] = fp4<2>(q.w, s); w[15] = fp4<3>(q.w, s);
   }
   // NVFP4: E2M1 exact, E4M3 scale on each 16-block's fp32 partial
-  static __device__ __forceinline__ void nvfp4(const uint8_t* __restrict__ qrow,
-                                               const uint8_t* __restrict__ srow, int c,
+  static __device__ __forceinline__ void nvfp4(const uint4 (&q)[KU], const uint32_t (&sc)[KU],
                                                const uint32_t (&x)[NT][KU][16], float (&acc)[NT]) {
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      const int u = c + LR * j;
-      const uint4 q = *reinterpret_cast<const uint4*>(qrow + 16 * u);
-      const uint32_t sc = *reinterpret_cast<const uint16_t*>(srow + 2 * u);
-      const float s0 = e4m3_to_f32<0>(sc);
-      const float s1 = e4m3_to_f32<1>(sc);
+      const float s0 = e4m3_to_f32<0>(sc[j]);
+      const float s1 = e4m3_to_f32<1>(sc[j]);
       uint32_t w[16];
-      fp4x16(q, 1.0f, w);
+      fp4x16(q[j], 1.0f, w);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         float p0 = 0.0f, p1 = 0.0f;
@@ -97,27 +135,23 @@ struct RowDot {
   }
   // MXFP4: bf16 folds the E8M0 exponent into the conversion (exact); fp16 cannot
   // hold that range, so there the exact fp32 2^(b - 127) scales the partial
-  static __device__ __forceinline__ void mxfp4(const uint8_t* __restrict__ qrow,
-                                               const uint8_t* __restrict__ srow, int c,
+  static __device__ __forceinline__ void mxfp4(const uint4 (&q)[KU], const uint32_t (&sc)[KU],
                                                const uint32_t (&x)[NT][KU][16], float (&acc)[NT]) {
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      const int u = c + LR * j;
-      const uint4 q = *reinterpret_cast<const uint4*>(qrow + 16 * u);
-      const uint32_t b = srow[u];
       uint32_t w[16];
       if constexpr (F16) {
-        fp4x16(q, 1.0f, w);
-        const float sc = e8m0_to_f32(b);
+        fp4x16(q[j], 1.0f, w);
+        const float s = e8m0_to_f32(sc[j]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           float p = 0.0f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) p = dot(w[i], x[t][j][i], p);
-          acc[t] = __builtin_fmaf(sc, p, acc[t]);
+          acc[t] = __builtin_fmaf(s, p, acc[t]);
         }
       } else {
-        fp4x16(q, e8m0_scale_operand(b), w);
+        fp4x16(q[j], e8m0_scale_operand(sc[j]), w);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -127,16 +161,13 @@ struct RowDot {
     }
   }
   // NF3: level pairs from the per-lane LDS table, fp16 group scale per 64
-  static __device__ __forceinline__ void nf3(const uint8_t* __restrict__ qrow,
-                                             const uint16_t* __restrict__ srow, int c,
+  static __device__ __forceinline__ void nf3(const uint4 (&q)[KU], const uint32_t (&sc)[KU],
                                              const uint32_t* __restrict__ lut_lane,
                                              const uint32_t (&x)[NT][KU][16], float (&acc)[NT]) {
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      const int u = c + LR * j;
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(qrow + 12 * u);
-      const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
-      const float s = fp16_to_f32(srow[u >> 1]);
+      const uint32_t d0 = q[j].x, d1 = q[j].y, d2 = q[j].z;
+      const float s = fp16_to_f32(sc[j]);
       uint32_t w[16];
       w[0] = lut_lane[nf3_pair_field<0>(d0, d1, d2) << 6];
       w[1] = lut_lane[nf3_pair_field<1>(d0, d1, d2) << 6];
@@ -165,134 +196,280 @@ struct RowDot {
   }
 };
 
-// One pass over the task's rows for NT (1 or 2) tokens; writes per-K-part row
-// results into res[kpart][row][t].
-template <int LR, int KU, int WK, int RI, int NT, bool W13>
-__device__ __forceinline__ void gemv_pass(const GemvArgs& a, bool nf3, int loc, int tile,
-                                          const uint32_t (&x)[NT][KU][16],
-                                          const uint32_t* __restrict__ lut_lane,
-                                          float (*res)[kMaxTaskRows][2]) {
-  constexpr bool F16 = !W13;
-  constexpr int P = kWave / LR;
-  constexpr int RG = 4 / WK;  // row groups
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int kpart = wave % WK;
-  const int rgroup = wave / WK;
-  const int c = lane % LR;
-  const int rw = lane / LR;
-  const int task_rows = W13 ? 2 * a.tile_rows : a.tile_rows;
-  const int Kp = a.K / WK;  // K-elements of this part
-  for (int r0 = rgroup * P * RI; r0 < task_rows; r0 += RG * P * RI) {
-    float acc[RI][NT];
+// Group d's record (one 48-byte load): tier, tier-local id and validated slot count
+// (0 when the grouping in scratch is stale or out of range). The slots themselves are
+// re-read per pass (slot_of): a register array indexed by the pass number would be
+// placed in private memory.
+struct ExpertInfo {
+  bool nf3;
+  int loc;
+  int n;
+  int d;
+};
+
+__device__ __forceinline__ ExpertInfo expert_info(const GemvArgs& a, int d) {
+  const int4* rp = reinterpret_cast<const int4*>(a.recs + d * kGroupRec);
+  const int4 r0 = rp[0], r1 = rp[1], r2 = rp[2];
+  const int sl[kDecodeMaxM] = {r1.x, r1.y, r1.z, r1.w, r2.x, r2.y, r2.z, r2.w};
+  ExpertInfo r;
+  r.d = d;
+  r.nf3 = (r0.y >> 16) != 0;
+  r.loc = r0.y & 0xFFFF;
+  int n = min(r0.z, kDecodeMaxM);
+  if ((unsigned)r0.x >= (unsigned)a.E || r.loc >= (r.nf3 ? a.E3 : a.E4)) n = 0;
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) {
+  for (int i = 0; i < kDecodeMaxM; ++i)
+    if (i < n && (unsigned)sl[i] >= (unsigned)a.nslot) n = 0;
+  r.n = n;
+  return r;
+}
+
+// slot of pass i (< ex.n, validated by expert_info)
+__device__ __forceinline__ int slot_of(const GemvArgs& a, const ExpertInfo& ex, int i) {
+  return a.recs[ex.d * kGroupRec + 4 + i];
+}
+
+// Weight formats of one segment; the dispatch happens once per expert segment so
+// every load and decode below is straight-line code.
+enum : int { kFmtNvfp4 = 0, kFmtMxfp4 = 1, kFmtNf3 = 2 };
+
+// Loads one row's KU units (codes + scale word) for this lane.
+template <int LR, int KU, int FMT>
+__device__ __forceinline__ void load_row(const GemvArgs& a, size_t grow, int c, uint4 (&q)[KU],
+                                         uint32_t (&sc)[KU]) {
+  if constexpr (FMT == kFmtNf3) {
+    const uint8_t* qrow = a.nq + grow * (3 * a.K / 8);
+    const uint16_t* srow = a.ns + grow * (a.K / 64);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[ri][t] = 0.0f;
-      const int rr = r0 + ri * P + rw;
-      const int row = W13 ? (rr < a.tile_rows ? tile * a.tile_rows + rr
-                                             : a.I + tile * a.tile_rows + (rr - a.tile_rows))
-                          : tile * a.tile_rows + rr;
-      const size_t grow = (size_t)loc * a.rows + row;
-      if (nf3) {
-        const uint8_t* qrow = a.nq + grow * (3 * a.K / 8) + (size_t)kpart * (3 * Kp / 8);
-        const uint16_t* srow = a.ns + grow * (a.K / 64) + kpart * (Kp / 64);
-        RowDot<LR, KU, NT, F16>::nf3(qrow, srow, c, lut_lane, x, acc[ri]);
-      } else if (a.kept_fmt == HMOE_KEPT_NVFP4) {
-        const uint8_t* qrow = a.kq + grow * (a.K / 2) + (size_t)kpart * (Kp / 2);
-        const uint8_t* srow = a.ks + grow * (a.K / 16) + kpart * (Kp / 16);
-        RowDot<LR, KU, NT, F16>::nvfp4(qrow, srow, c, x, acc[ri]);
-      } else {
-        const uint8_t* qrow = a.kq + grow * (a.K / 2) + (size_t)kpart * (Kp / 2);
-        const uint8_t* srow = a.ks + grow * (a.K / 32) + kpart * (Kp / 32);
-        RowDot<LR, KU, NT, F16>::mxfp4(qrow, srow, c, x, acc[ri]);
-      }
+    for (int j = 0; j < KU; ++j) {
+      const int u = c + LR * j;
+      const uint3 v = *reinterpret_cast<const uint3*>(qrow + 12 * u);
+      q[j] = make_uint4(v.x, v.y, v.z, 0u);
+      sc[j] = srow[u >> 1];
     }
+  } else if constexpr (FMT == kFmtNvfp4) {
+    const uint8_t* qrow = a.kq + grow * (a.K / 2);
+    const uint8_t* srow = a.ks + grow * (a.K / 16);
 #pragma unroll
-    for (int ri = 0; ri < RI; ++ri) {
-      const int rr = r0 + ri * P + rw;
+    for (int j = 0; j < KU; ++j) {
+      const int u = c + LR * j;
+      q[j] = *reinterpret_cast<const uint4*>(qrow + 16 * u);
+      sc[j] = *reinterpret_cast<const uint16_t*>(srow + 2 * u);
+    }
+  } else {
+    const uint8_t* qrow = a.kq + grow * (a.K / 2);
+    const uint8_t* srow = a.ks + grow * (a.K / 32);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float v = group_sum<LR>(acc[ri][t]);
-        if (c == 0) res[kpart][rr][t] = v;
-      }
+    for (int j = 0; j < KU; ++j) {
+      const int u = c + LR * j;
+      q[j] = *reinterpret_cast<const uint4*>(qrow + 16 * u);
+      sc[j] = srow[u];
     }
   }
 }
 
-// W13 activations: the lane's x units of up to two tokens as bf16 pairs.
-template <int LR, int KU, int WK, int NT>
-__device__ __forceinline__ void load_act_bf16(const GemvArgs& a, int s0, int s1,
-                                              uint32_t (&x)[NT][KU][16]) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int kpart = (threadIdx.x >> 6) % WK;
-  const int c = lane % LR;
-  const int Kp = a.K / WK;
+template <int LR, int KU, int NT, bool F16, int FMT>
+__device__ __forceinline__ void row_dot(const uint4 (&q)[KU], const uint32_t (&sc)[KU],
+                                        const uint32_t* lut_lane,
+                                        const uint32_t (&x)[NT][KU][16], float (&acc)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
+  if constexpr (FMT == kFmtNf3) RowDot<LR, KU, NT, F16>::nf3(q, sc, lut_lane, x, acc);
+  else if constexpr (FMT == kFmtNvfp4) RowDot<LR, KU, NT, F16>::nvfp4(q, sc, x, acc);
+  else RowDot<LR, KU, NT, F16>::mxfp4(q, sc, x, acc);
+}
+
+// Calls f with the segment's format as a compile-time constant.
+template <typename F>
+__device__ __forceinline__ void with_format(const GemvArgs& a, const ExpertInfo& ex, F&& f) {
+  if (ex.nf3) f(std::integral_constant<int, kFmtNf3>{});
+  else if (a.kept_fmt == HMOE_KEPT_NVFP4) f(std::integral_constant<int, kFmtNvfp4>{});
+  else f(std::integral_constant<int, kFmtMxfp4>{});
+}
+
+// ---------------------------------------------------------------------------
+// W13 + SwiGLU
+// ---------------------------------------------------------------------------
+
+// x units of up to NT tokens (bf16 pairs) for this lane
+template <int LR, int KU, int NT>
+__device__ __forceinline__ void load_x(const GemvArgs& a, const int (&slot)[NT], int c,
+                                       uint32_t (&x)[NT][KU][16]) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int s = t == 0 ? s0 : s1;
-    const uint16_t* row = a.act_bf16 + (size_t)(s / a.act_row_div) * a.K + (size_t)kpart * Kp;
+    const uint16_t* row = a.act_bf16 + (size_t)(slot[t] / a.k) * a.K;
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
       const uint4* p = reinterpret_cast<const uint4*>(row + 32 * (c + LR * j));
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const uint4 q = p[v];
-        x[t][j][4 * v + 0] = q.x;
-        x[t][j][4 * v + 1] = q.y;
-        x[t][j][4 * v + 2] = q.z;
-        x[t][j][4 * v + 3] = q.w;
+        const uint4 qv = p[v];
+        x[t][j][4 * v + 0] = qv.x;
+        x[t][j][4 * v + 1] = qv.y;
+        x[t][j][4 * v + 2] = qv.z;
+        x[t][j][4 * v + 3] = qv.w;
       }
     }
   }
 }
 
-// W2 activations: the lane's h units (fp32) of up to two slots, scaled by 2^-e[t]
-// with e[t] chosen from the slot's largest |h| (over the whole row, reduced across
-// the block) and rounded to fp16 pairs. The row is read twice (max, then convert);
-// it is a few KB and cache-resident. Every thread of the block must call this.
-template <int LR, int KU, int WK, int NT>
-__device__ __forceinline__ void load_act_f16(const GemvArgs& a, int s0, int s1,
-                                             uint32_t (&x)[NT][KU][16], int (&e)[NT],
-                                             float (*s_max)[2]) {
+// Weights of one W13 chunk (P * RI row pairs) for this lane: gate and up rows.
+template <int KU, int RI>
+struct W13Buf {
+  uint4 qg[RI][KU], qu[RI][KU];
+  uint32_t sg[RI][KU], su[RI][KU];
+};
+
+template <int LR, int KU, int RI, int FMT>
+__device__ __forceinline__ void w13_load(const GemvArgs& a, int loc, int i0, W13Buf<KU, RI>& b) {
+  constexpr int P = kWave / LR;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  const int kpart = wave % WK;
   const int c = lane % LR;
-  const int Kp = a.K / WK;
-  const float* rows[NT];
-  float mx[NT];
+  const int rw = lane / LR;
+  const size_t base = (size_t)loc * a.rows;
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    const int i = i0 + ri * P + rw;
+    load_row<LR, KU, FMT>(a, base + i, c, b.qg[ri], b.sg[ri]);
+    load_row<LR, KU, FMT>(a, base + a.I + i, c, b.qu[ri], b.su[ri]);
+  }
+}
+
+template <int LR, int KU, int RI, int NT, int FMT>
+__device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, const int (&slot)[NT],
+                                            float g, const uint32_t (&x)[NT][KU][16],
+                                            const uint32_t* lut_lane, const W13Buf<KU, RI>& b) {
+  constexpr int P = kWave / LR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane % LR;
+  const int rw = lane / LR;
+  float vg[RI * NT], vu[RI * NT];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    float ag[NT], au[NT];
+    row_dot<LR, KU, NT, false, FMT>(b.qg[ri], b.sg[ri], lut_lane, x, ag);
+    row_dot<LR, KU, NT, false, FMT>(b.qu[ri], b.su[ri], lut_lane, x, au);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      vg[ri * NT + t] = ag[t];
+      vu[ri * NT + t] = au[t];
+    }
+  }
+  constexpr int V = RI * NT;
+  const float gate = seg_reduce<V, LR>(vg) * g;
+  const float up = seg_reduce<V, LR>(vu) * g;
+  const int o = seg_index<V, LR>(c);
+  if ((c & (LR / V - 1)) == 0) {
+    const int ri = o / NT;
+    const int t = o - ri * NT;
+    a.h_out[(size_t)slot[t] * a.I + i0 + ri * P + rw] = silu(gate) * up;
+  }
+}
+
+// Chunks [c0, end) of one expert (chunk `first` is its pair 0), once per token of
+// the group: the next chunk's weights are in flight while the current one is
+// computed. A holds chunk c0 on entry when a_loaded.
+template <int LR, int KU, int RI, int FMT>
+__device__ __forceinline__ void w13_segment(const GemvArgs& a, const ExpertInfo& ex, int c0,
+                                            int end, int first, float g,
+                                            const uint32_t* lut_lane, W13Buf<KU, RI>& A,
+                                            W13Buf<KU, RI>& B, bool a_loaded) {
+  constexpr int CH = (kWave / LR) * RI;
+  const int c = (threadIdx.x & (kWave - 1)) % LR;
+  for (int p = 0; p < ex.n; ++p) {
+    const int slot[1] = {slot_of(a, ex, p)};
+    int cc = c0;
+    if (!(a_loaded && p == 0)) w13_load<LR, KU, RI, FMT>(a, ex.loc, (cc - first) * CH, A);
+    uint32_t x[1][KU][16];
+    load_x<LR, KU, 1>(a, slot, c, x);
+    while (cc < end) {
+      if (cc + 1 < end) w13_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, B);
+      w13_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, A);
+      if (++cc >= end) break;
+      if (cc + 1 < end) w13_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, A);
+      w13_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, B);
+      ++cc;
+    }
+  }
+}
+
+template <int LR, int KU, int RI>
+__global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
+  __shared__ uint32_t lut[64 * kWave];  // [pair field][lane]: bf16 pair of scaled NF3 levels
+  constexpr int P = kWave / LR;
+  constexpr int CH = P * RI;  // pairs per chunk
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t* lut_lane = lut + lane;
+  const int nd = min(a.counts[0], a.bound);
+  const int per_expert = a.out_units / CH;
+  const int total = nd * per_expert;
+  const int nw = gridDim.x * kGemvWaves;
+  // wave-uniform (scalar) from here on: the range, the expert, its tier and slots
+  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c_begin = (int)((long)gw * total / nw), c_end = (int)((long)(gw + 1) * total / nw);
+  // the first chunk's weights are requested before the table is built
+  W13Buf<KU, RI> A, B;
+  ExpertInfo ex{};
+  if (c_begin < c_end) {
+    ex = expert_info(a, c_begin / per_expert);
+    if (ex.n > 0)
+      with_format(a, ex, [&](auto f) {
+        w13_load<LR, KU, RI, decltype(f)::value>(a, ex.loc, (c_begin % per_expert) * CH, A);
+      });
+  }
+  for (int i = threadIdx.x; i < 64 * kWave; i += kGemvThreads) {
+    const int f = i / kWave;
+    lut[i] = pack_bf16(nf3_level(f & 7) * kNF3TableScaleBf16, nf3_level(f >> 3) * kNF3TableScaleBf16);
+  }
+  __syncthreads();
+  int ch = c_begin;
+  bool first_seg = true;
+  while (ch < c_end) {
+    const int d = ch / per_expert;
+    const int d_end = min(c_end, (d + 1) * per_expert);
+    if (!first_seg) ex = expert_info(a, d);
+    const float g = ex.nf3 ? 1.0f / kNF3TableScaleBf16
+                           : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[ex.loc] : 1.0f);
+    // one token per pass: a second token re-streams this range from cache
+    with_format(a, ex, [&](auto f) {
+      w13_segment<LR, KU, RI, decltype(f)::value>(a, ex, ch, d_end, d * per_expert, g, lut_lane,
+                                                  A, B, first_seg);
+    });
+    first_seg = false;
+    ch = d_end;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// W2
+// ---------------------------------------------------------------------------
+
+// h units of up to NT slots, scaled by 2^-e[t] (e from the slot's largest |h| over
+// the whole row; every LR-lane segment of the wave covers the full row) and rounded
+// to fp16 pairs
+template <int LR, int KU, int NT>
+__device__ __forceinline__ void load_h(const GemvArgs& a, const int (&slot)[NT], int c,
+                                       uint32_t (&x)[NT][KU][16], int (&e)[NT]) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const int s = t == 0 ? s0 : s1;
-    rows[t] = a.act_f32 + (size_t)(s / a.act_row_div) * a.K + (size_t)kpart * Kp;
-    mx[t] = 0.0f;
+    const float* row = a.act_f32 + (size_t)slot[t] * a.K;
+    float mx = 0.0f;
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      const float4* p = reinterpret_cast<const float4*>(rows[t] + 32 * (c + LR * j));
+      const float4* p = reinterpret_cast<const float4*>(row + 32 * (c + LR * j));
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const float4 q = p[v];
-        mx[t] = fmaxf(mx[t], fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
       }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx[t] = fmaxf(mx[t], __shfl_xor(mx[t], off));
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) s_max[wave][t] = mx[t];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float m = fmaxf(fmaxf(s_max[0][t], s_max[1][t]), fmaxf(s_max[2][t], s_max[3][t]));
+    mx = group_max<LR>(mx);
     // scale so that max * 2^-e lands in [2^14, 2^15), inside fp16's range
-    const int ef = (int)((__float_as_uint(m) >> 23) & 0xFF);
-    e[t] = m > 0.0f ? (ef == 0 ? -126 : ef - 127) - 14 : 0;
+    const int ef = (int)((__float_as_uint(mx) >> 23) & 0xFF);
+    e[t] = mx > 0.0f ? (ef == 0 ? -126 : ef - 127) - 14 : 0;
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      const float4* p = reinterpret_cast<const float4*>(rows[t] + 32 * (c + LR * j));
+      const float4* p = reinterpret_cast<const float4*>(row + 32 * (c + LR * j));
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         const float4 q = p[v];
@@ -301,88 +478,118 @@ __device__ __forceinline__ void load_act_f16(const GemvArgs& a, int s0, int s1,
       }
     }
   }
-  __syncthreads();
 }
 
-template <int LR, int KU, int WK, int RI, bool W13>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(GemvArgs a) {
-  __shared__ uint32_t lut[64 * kWave];  // [pair field][lane]: 16-bit pair of scaled NF3 levels
-  __shared__ float res[WK][kMaxTaskRows][2];
-  __shared__ float s_max[4][2];
-  for (int i = threadIdx.x; i < 64 * kWave; i += kGemvThreads) {
-    const int f = i / kWave;
-    if (W13)
-      lut[i] = pack_bf16(nf3_level(f & 7) * kNF3TableScaleBf16, nf3_level(f >> 3) * kNF3TableScaleBf16);
-    else
-      lut[i] = pack_f16(nf3_level(f & 7) * kNF3TableScaleF16, nf3_level(f >> 3) * kNF3TableScaleF16);
+template <int KU, int RI>
+struct W2Buf {
+  uint4 q[RI][KU];
+  uint32_t sc[RI][KU];
+};
+
+template <int LR, int KU, int RI, int FMT>
+__device__ __forceinline__ void w2_load(const GemvArgs& a, int loc, int n0, W2Buf<KU, RI>& b) {
+  constexpr int P = kWave / LR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane % LR;
+  const int rw = lane / LR;
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri)
+    load_row<LR, KU, FMT>(a, (size_t)loc * a.rows + n0 + ri * P + rw, c, b.q[ri], b.sc[ri]);
+}
+
+template <int LR, int KU, int RI, int NT, int FMT>
+__device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, const int (&slot)[NT],
+                                           const float (&g)[NT], const uint32_t (&x)[NT][KU][16],
+                                           const uint32_t* lut_lane, const W2Buf<KU, RI>& b) {
+  constexpr int P = kWave / LR;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int c = lane % LR;
+  const int rw = lane / LR;
+  float v[RI * NT];
+#pragma unroll
+  for (int ri = 0; ri < RI; ++ri) {
+    float acc[NT];
+    row_dot<LR, KU, NT, true, FMT>(b.q[ri], b.sc[ri], lut_lane, x, acc);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[ri * NT + t] = acc[t];
   }
-  __syncthreads();
+  constexpr int V = RI * NT;
+  const float sum = seg_reduce<V, LR>(v);
+  const int o = seg_index<V, LR>(c);
+  if ((c & (LR / V - 1)) == 0) {
+    const int ri = o / NT;
+    const int t = o - ri * NT;
+    a.o_out[(size_t)slot[t] * a.rows + n0 + ri * P + rw] = sum * g[t];
+  }
+}
+
+template <int LR, int KU, int RI, int FMT>
+__device__ __forceinline__ void w2_segment(const GemvArgs& a, const ExpertInfo& ex, int c0,
+                                           int end, int first, float gt,
+                                           const uint32_t* lut_lane, W2Buf<KU, RI>& A,
+                                           W2Buf<KU, RI>& B, bool a_loaded) {
+  constexpr int CH = (kWave / LR) * RI;
+  const int c = (threadIdx.x & (kWave - 1)) % LR;
+  for (int p = 0; p < ex.n; ++p) {
+    const int slot[1] = {slot_of(a, ex, p)};
+    int cc = c0;
+    if (!(a_loaded && p == 0)) w2_load<LR, KU, RI, FMT>(a, ex.loc, (cc - first) * CH, A);
+    uint32_t x[1][KU][16];
+    int e[1];
+    load_h<LR, KU, 1>(a, slot, c, x, e);
+    const float g[1] = {__builtin_ldexpf(gt, e[0])};
+    while (cc < end) {
+      if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, B);
+      w2_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, A);
+      if (++cc >= end) break;
+      if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, A);
+      w2_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, B);
+      ++cc;
+    }
+  }
+}
+
+template <int LR, int KU, int RI>
+__global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
+  __shared__ uint32_t lut[64 * kWave];  // [pair field][lane]: fp16 pair of scaled NF3 levels
+  constexpr int P = kWave / LR;
+  constexpr int CH = P * RI;  // rows per chunk
   const int lane = threadIdx.x & (kWave - 1);
   const uint32_t* lut_lane = lut + lane;
-  const int ntask = a.counts[0] * a.tiles;
-  for (int task = blockIdx.x; task < ntask; task += gridDim.x) {
-    const int d = task / a.tiles;
-    const int tile = task - d * a.tiles;
-    const int e = a.experts[d];
-    const int tc = a.expert_tier[e];
-    const bool nf3 = (tc >> 16) != 0;
-    const int loc = tc & 0xFFFF;
-    const int n = a.nslots[d];
-    // per-row factor: NVFP4 per-tensor scale, or 1/c of the scaled NF3 table
-    float g = 1.0f;
-    if (nf3) g = 1.0f / (W13 ? kNF3TableScaleBf16 : kNF3TableScaleF16);
-    else if (a.kept_fmt == HMOE_KEPT_NVFP4) g = a.kg[loc];
-    for (int p0 = 0; p0 < n; p0 += 2) {
-      const int nt = n - p0 >= 2 ? 2 : 1;
-      const int s0 = a.slots[d * kDecodeMaxM + p0];
-      const int s1 = nt == 2 ? a.slots[d * kDecodeMaxM + p0 + 1] : s0;
-      int ex[2] = {0, 0};
-      if (nt == 2) {
-        uint32_t x[2][KU][16];
-        if constexpr (W13) {
-          load_act_bf16<LR, KU, WK, 2>(a, s0, s1, x);
-        } else {
-          int e2[2];
-          load_act_f16<LR, KU, WK, 2>(a, s0, s1, x, e2, s_max);
-          ex[0] = e2[0];
-          ex[1] = e2[1];
-        }
-        gemv_pass<LR, KU, WK, RI, 2, W13>(a, nf3, loc, tile, x, lut_lane, res);
-      } else {
-        uint32_t x[1][KU][16];
-        if constexpr (W13) {
-          load_act_bf16<LR, KU, WK, 1>(a, s0, s1, x);
-        } else {
-          int e1[1];
-          load_act_f16<LR, KU, WK, 1>(a, s0, s1, x, e1, s_max);
-          ex[0] = e1[0];
-        }
-        gemv_pass<LR, KU, WK, RI, 1, W13>(a, nf3, loc, tile, x, lut_lane, res);
-      }
-      __syncthreads();
-      for (int idx = threadIdx.x; idx < a.tile_rows * nt; idx += kGemvThreads) {
-        const int t = idx / a.tile_rows;
-        const int i = idx - t * a.tile_rows;
-        const int slot = t == 0 ? s0 : s1;
-        if (W13) {
-          float gate = 0.0f, up = 0.0f;
-#pragma unroll
-          for (int kp = 0; kp < WK; ++kp) {
-            gate += res[kp][i][t];
-            up += res[kp][a.tile_rows + i][t];
-          }
-          gate *= g;
-          up *= g;
-          a.h_out[(size_t)slot * a.I + tile * a.tile_rows + i] = silu(gate) * up;
-        } else {
-          float o = 0.0f;
-#pragma unroll
-          for (int kp = 0; kp < WK; ++kp) o += res[kp][i][t];
-          a.o_out[(size_t)slot * a.rows + tile * a.tile_rows + i] = __builtin_ldexpf(o * g, ex[t]);
-        }
-      }
-      __syncthreads();
-    }
+  const int nd = min(a.counts[0], a.bound);
+  const int per_expert = a.out_units / CH;
+  const int total = nd * per_expert;
+  const int nw = gridDim.x * kGemvWaves;
+  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c_begin = (int)((long)gw * total / nw), c_end = (int)((long)(gw + 1) * total / nw);
+  W2Buf<KU, RI> A, B;
+  ExpertInfo ex{};
+  if (c_begin < c_end) {
+    ex = expert_info(a, c_begin / per_expert);
+    if (ex.n > 0)
+      with_format(a, ex, [&](auto f) {
+        w2_load<LR, KU, RI, decltype(f)::value>(a, ex.loc, (c_begin % per_expert) * CH, A);
+      });
+  }
+  for (int i = threadIdx.x; i < 64 * kWave; i += kGemvThreads) {
+    const int f = i / kWave;
+    lut[i] = pack_f16(nf3_level(f & 7) * kNF3TableScaleF16, nf3_level(f >> 3) * kNF3TableScaleF16);
+  }
+  __syncthreads();
+  int ch = c_begin;
+  bool first_seg = true;
+  while (ch < c_end) {
+    const int d = ch / per_expert;
+    const int d_end = min(c_end, (d + 1) * per_expert);
+    if (!first_seg) ex = expert_info(a, d);
+    const float gt = ex.nf3 ? 1.0f / kNF3TableScaleF16
+                            : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[ex.loc] : 1.0f);
+    with_format(a, ex, [&](auto f) {
+      w2_segment<LR, KU, RI, decltype(f)::value>(a, ex, ch, d_end, d * per_expert, gt, lut_lane,
+                                                 A, B, first_seg);
+    });
+    first_seg = false;
+    ch = d_end;
   }
 }
 
@@ -395,8 +602,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   if (idx >= M * H) return;
   const int t = idx / H;
   const int n = idx - t * H;
+  float ov[kMaxTopK], wv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {   // all loads first, then the fixed-order sum
+    ov[j] = j < k ? o[(size_t)(t * k + j) * H + n] : 0.0f;
+    wv[j] = j < k ? w[t * k + j] : 0.0f;
+  }
   float acc = 0.0f;
-  for (int j = 0; j < k; ++j) acc = __builtin_fmaf(w[t * k + j], o[(size_t)(t * k + j) * H + n], acc);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) acc = __builtin_fmaf(wv[j], ov[j], acc);
   y[idx] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
 }
 
@@ -407,105 +621,128 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 typedef void (*GemvFn)(GemvArgs);
 
 template <bool W13>
-static GemvFn pick_gemv(const GemvTiling& t, int wk) {
-#define HMOE_GEMV_CASE(LR_, KU_, WK_)                                         \
-  if (t.lr == LR_ && t.ku == KU_ && wk == WK_)                               \
-    return gemv_kernel<LR_, KU_, WK_, (KU_ == 1 ? 4 : 2), W13>;
-#define HMOE_GEMV_LR(LR_, WK_) \
-  HMOE_GEMV_CASE(LR_, 1, WK_) HMOE_GEMV_CASE(LR_, 2, WK_) HMOE_GEMV_CASE(LR_, 3, WK_)
-  HMOE_GEMV_LR(64, 1) HMOE_GEMV_LR(32, 1) HMOE_GEMV_LR(16, 1) HMOE_GEMV_LR(8, 1) HMOE_GEMV_LR(4, 1)
-  HMOE_GEMV_LR(64, 4) HMOE_GEMV_LR(32, 4) HMOE_GEMV_LR(16, 4) HMOE_GEMV_LR(8, 4) HMOE_GEMV_LR(4, 4)
-#undef HMOE_GEMV_LR
+static GemvFn pick_gemv(const GemvTiling& t) {
+#define HMOE_GEMV_CASE(LR_, KU_, RI_)                                            \
+  if (t.lr == LR_ && t.ku == KU_ && t.ri == RI_) {                              \
+    if constexpr (W13) return w13_gemv_kernel<LR_, KU_, RI_>;                   \
+    else return w2_gemv_kernel<LR_, KU_, RI_>;                                  \
+  }
+  HMOE_GEMV_CASE(64, 1, 4) HMOE_GEMV_CASE(64, 2, 2) HMOE_GEMV_CASE(64, 3, 1) HMOE_GEMV_CASE(64, 4, 1)
+  HMOE_GEMV_CASE(32, 1, 4) HMOE_GEMV_CASE(32, 2, 2) HMOE_GEMV_CASE(32, 3, 1) HMOE_GEMV_CASE(32, 4, 1)
+  HMOE_GEMV_CASE(16, 1, 4) HMOE_GEMV_CASE(16, 2, 2) HMOE_GEMV_CASE(16, 3, 1) HMOE_GEMV_CASE(16, 4, 1)
+  HMOE_GEMV_CASE(8, 1, 4) HMOE_GEMV_CASE(8, 2, 2) HMOE_GEMV_CASE(8, 3, 1) HMOE_GEMV_CASE(8, 4, 1)
+  HMOE_GEMV_CASE(4, 1, 2) HMOE_GEMV_CASE(4, 2, 2) HMOE_GEMV_CASE(4, 3, 1) HMOE_GEMV_CASE(4, 4, 1)
 #undef HMOE_GEMV_CASE
   return nullptr;
 }
 
-// WK for a GEMV over K: split K across the 4 waves when each part still gives a
-// wave at least 16 units of 32 elements and holds whole NF3 groups of 64.
-static int gemv_wk(int K) {
+// Decode GEMV tiling over reduction length K: LR = the largest power of two up to 64
+// dividing the K/32 units, KU = units per lane, RI = rows (or row pairs) per lane per
+// chunk, bounded so the values a lane reduces (RI * 2 tokens per reduction) never
+// outnumber the lanes of its LR-lane segment.
+bool plan_gemv(int K, GemvTiling* t) {
   const int U = K / 32;
-  return (U % 8 == 0 && U / 4 >= 16) ? 4 : 1;
+  int lr = 1;
+  while (lr < 64 && U % (2 * lr) == 0) lr *= 2;
+  const int ku = U / lr;
+  if (lr < 4 || ku < 1 || ku > 4) return false;
+  int ri = ku == 1 ? 4 : (ku == 2 ? 2 : 1);
+  while (ri * 2 > lr) ri /= 2;
+  if (ri < 1) return false;
+  t->lr = lr;
+  t->ku = ku;
+  t->ri = ri;
+  return true;
+}
+
+// blocks of one GEMV kernel resident per CU (occupancy query, cached per kernel)
+static int resident_blocks(GemvFn fn) {
+  static GemvFn fns[16] = {};
+  static int counts[16] = {};
+  for (int i = 0; i < 16; ++i) {
+    if (fns[i] == fn) return counts[i];
+    if (fns[i] == nullptr) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
+                                                       kGemvThreads, 0) != hipSuccess || n < 1)
+        n = 2;
+      fns[i] = fn;
+      counts[i] = n;
+      return n;
+    }
+  }
+  return 2;
+}
+
+static int cu_count() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cached = n;
+    else
+      cached = 256;
+  }
+  return cached;
 }
 
 hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
-                         uint16_t* y, void* scratch, hipStream_t s) {
+                         uint16_t* y, void* scratch, int stage, hipStream_t s) {
   char* base = static_cast<char*>(scratch);
   const ScratchPlan& P = L.plan;
   GemvArgs a{};
   a.kept_fmt = L.kept_format;
   a.counts = reinterpret_cast<const int32_t*>(base + P.d_counts);
-  a.experts = reinterpret_cast<const int32_t*>(base + P.d_experts);
-  a.nslots = reinterpret_cast<const int32_t*>(base + P.d_nslots);
-  a.slots = reinterpret_cast<const int32_t*>(base + P.d_slots);
-  a.expert_tier = reinterpret_cast<const int32_t*>(base + P.expert_tier);
+  a.recs = reinterpret_cast<const int32_t*>(base + P.d_recs);
   a.I = L.I;
+  a.E = L.E;
+  a.E4 = L.E4;
+  a.E3 = L.E3;
+  a.k = L.k;
+  a.nslot = M * L.k;
+  a.bound = (M * L.k < L.max_distinct) ? M * L.k : L.max_distinct;
   float* h = reinterpret_cast<float*>(base + P.h_dec);
   float* o = reinterpret_cast<float*>(base + P.o_dec);
-  const int bound = (M * L.k < L.E) ? M * L.k : L.E;  // distinct experts at most
-
-  // W13 + SwiGLU
-  {
+  // a persistent grid: as many blocks as fit on the GPU at once, never more waves
+  // than chunks
+  auto grid_for = [&](GemvFn fn, const GemvTiling& t, int out_units) {
+    const long chunks = (long)a.bound * (out_units / ((64 / t.lr) * t.ri));
+    const long blocks = (chunks + kGemvWaves - 1) / kGemvWaves;
+    const long cap = (long)resident_blocks(fn) * cu_count();
+    return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
+  };
+  if (stage == HMOE_STAGE_W13) {
     GemvArgs b = a;
     b.kq = W.kept_w13_q; b.ks = W.kept_w13_s; b.kg = W.kept_w13_g;
     b.nq = W.nf3_w13_q; b.ns = W.nf3_w13_s;
-    b.rows = 2 * L.I; b.K = L.H;
-    b.act_bf16 = x; b.act_row_div = L.k;
-    b.tile_rows = L.w13.rows_per_task;
-    b.tiles = L.I / b.tile_rows;
+    b.rows = 2 * L.I; b.K = L.H; b.out_units = L.I;
+    b.act_bf16 = x;
     b.h_out = h;
-    GemvFn fn = pick_gemv<true>(L.w13, gemv_wk(L.H));
+    GemvFn fn = pick_gemv<true>(L.w13);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(b.tiles * bound), dim3(kGemvThreads), 0, s, b);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(fn, dim3(grid_for(fn, L.w13, L.I)), dim3(kGemvThreads), 0, s, b);
+    return hipGetLastError();
   }
-  // W2
-  {
+  if (stage == HMOE_STAGE_W2) {
     GemvArgs b = a;
     b.kq = W.kept_w2_q; b.ks = W.kept_w2_s; b.kg = W.kept_w2_g;
     b.nq = W.nf3_w2_q; b.ns = W.nf3_w2_s;
-    b.rows = L.H; b.K = L.I;
-    b.act_f32 = h; b.act_row_div = 1;
-    b.tile_rows = L.w2.rows_per_task;
-    b.tiles = L.H / b.tile_rows;
+    b.rows = L.H; b.K = L.I; b.out_units = L.H;
+    b.act_f32 = h;
     b.o_out = o;
-    GemvFn fn = pick_gemv<false>(L.w2, gemv_wk(L.I));
+    GemvFn fn = pick_gemv<false>(L.w2);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(b.tiles * bound), dim3(kGemvThreads), 0, s, b);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(fn, dim3(grid_for(fn, L.w2, L.H)), dim3(kGemvThreads), 0, s, b);
+    return hipGetLastError();
   }
-  const int n = M * L.H;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, o,
-                     reinterpret_cast<const float*>(base + P.topk_w), M, L.k, L.H, y);
-  return hipGetLastError();
-}
-
-// Decode tiling of a GEMV over K with `out_rows` output rows per expert: lanes per
-// row and units per lane, and the rows per task (a multiple of what one block
-// iteration covers, dividing `out_rows`, at least `min_rows`).
-bool plan_gemv(int K, int out_rows, bool w13, int min_rows, GemvTiling* t) {
-  const int wk = gemv_wk(K);
-  const int U = K / 32 / wk;
-  int lr = 1;
-  while (lr < 64 && U % (2 * lr) == 0) lr *= 2;
-  const int ku = U / lr;
-  if (lr < 4 || ku < 1 || ku > 3) return false;
-  const int P = 64 / lr;
-  const int ri = ku == 1 ? 4 : 2;
-  const int per_iter = (4 / wk) * P * ri;  // task rows covered per block iteration
-  // W13 tasks hold tile_rows gate rows plus tile_rows up rows
-  const int step = w13 ? (per_iter % 2 == 0 ? per_iter / 2 : per_iter) : per_iter;
-  int rows = step;
-  while (rows < min_rows || out_rows % rows != 0) {
-    rows += step;
-    if (rows > out_rows || (w13 ? 2 * rows : rows) > kMaxTaskRows) return false;
+  if (stage == HMOE_STAGE_COMBINE) {
+    const int n = M * L.H;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, o,
+                       reinterpret_cast<const float*>(base + P.topk_w), M, L.k, L.H, y);
+    return hipGetLastError();
   }
-  if ((w13 ? 2 * rows : rows) > kMaxTaskRows) return false;
-  t->lr = lr;
-  t->ku = ku;
-  t->rows_per_task = rows;
-  return true;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hmoe

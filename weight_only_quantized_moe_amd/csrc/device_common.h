@@ -137,12 +137,71 @@ __device__ __forceinline__ uint32_t nf3_pair_field(uint32_t d0, uint32_t d1, uin
 }
 
 // ---------------------------------------------------------------------------
-// wave reductions (64 lanes); WIDTH-lane groups must be aligned powers of two
+// cross-lane exchange without the LDS crossbar
 // ---------------------------------------------------------------------------
+// xlane<B>(v) returns v from the partner lane of a butterfly step on lane bit B:
+// lane ^ 1, ^ 3, ^ 7, ^ 15 (DPP quad permute, row half-mirror, row mirror) for B <= 8,
+// lane ^ 16 and lane ^ 32 (v_permlane16_swap / v_permlane32_swap plus a select). Each
+// partner differs from the lane in bit B and only below it, so a sequence of steps over
+// B = LR/2 .. 1 visits every lane of an aligned LR-lane segment exactly once.
+template <int B>
+__device__ __forceinline__ uint32_t xlane_u32(uint32_t v) {
+  static_assert(B == 1 || B == 2 || B == 4 || B == 8 || B == 16 || B == 32, "butterfly bit");
+  if constexpr (B == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+  } else if constexpr (B == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false);   // quad [3,2,1,0]
+  } else if constexpr (B == 4) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // row half-mirror
+  } else if constexpr (B == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // row mirror
+  } else if constexpr (B == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+
+template <int B>
+__device__ __forceinline__ float xlane(float v) {
+  return __uint_as_float(xlane_u32<B>(__float_as_uint(v)));
+}
+
+template <int B>
+__device__ __forceinline__ int xlane_i(int v) {
+  return (int)xlane_u32<B>((uint32_t)v);
+}
+
+template <int B>
+__device__ __forceinline__ double xlane_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = xlane_u32<B>((uint32_t)u);
+  const uint64_t hi = xlane_u32<B>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+// sum / max over aligned WIDTH-lane groups (every lane of the group gets the result)
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, WIDTH);
+  if constexpr (WIDTH >= 64) v += xlane<32>(v);
+  if constexpr (WIDTH >= 32) v += xlane<16>(v);
+  if constexpr (WIDTH >= 16) v += xlane<8>(v);
+  if constexpr (WIDTH >= 8) v += xlane<4>(v);
+  if constexpr (WIDTH >= 4) v += xlane<2>(v);
+  if constexpr (WIDTH >= 2) v += xlane<1>(v);
+  return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (WIDTH >= 64) v = fmaxf(v, xlane<32>(v));
+  if constexpr (WIDTH >= 32) v = fmaxf(v, xlane<16>(v));
+  if constexpr (WIDTH >= 16) v = fmaxf(v, xlane<8>(v));
+  if constexpr (WIDTH >= 8) v = fmaxf(v, xlane<4>(v));
+  if constexpr (WIDTH >= 4) v = fmaxf(v, xlane<2>(v));
+  if constexpr (WIDTH >= 2) v = fmaxf(v, xlane<1>(v));
   return v;
 }
 

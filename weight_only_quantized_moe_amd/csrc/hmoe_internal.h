@@ -16,11 +16,13 @@ namespace hmoe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kDecodeMaxM = HMOE_DECODE_MAX_M;
+// decode group record (int32 words): expert id, tier code, slot count, 0, slots[8], 0 x 4
+constexpr int kGroupRec = 16;
 
 // Byte offsets of every scratch region (each 256-byte aligned).
 struct ScratchPlan {
   size_t topk_ids = 0, topk_w = 0, expert_tier = 0;
-  size_t d_counts = 0, d_experts = 0, d_nslots = 0, d_slots = 0;
+  size_t d_counts = 0, d_experts = 0, d_nslots = 0, d_slots = 0, d_recs = 0;
   size_t h_dec = 0, o_dec = 0;
   size_t a_counts = 0;                     // int32 [E] slot counts per expert
   size_t a_slots[2] = {0, 0}, a_bexp[2] = {0, 0}, a_eoff[2] = {0, 0}, a_npad[2] = {0, 0};
@@ -29,9 +31,9 @@ struct ScratchPlan {
 };
 
 // GEMV tiling of one weight tensor on the decode path: lanes per row (LR), units of
-// 32 K-elements per lane (KU), rows per task.
+// 32 K-elements per lane (KU), rows (or row pairs) per lane per chunk (RI).
 struct GemvTiling {
-  int lr = 0, ku = 0, rows_per_task = 0;
+  int lr = 0, ku = 0, ri = 0;
 };
 
 struct Layer {
@@ -64,18 +66,20 @@ hipError_t launch_route_group(const Layer& L, const float* logits, int M, void* 
 // align.hip
 hipError_t launch_align(const Layer& L, const int32_t* ids, int M, void* scratch, hipStream_t s);
 
-// decode.hip
+// decode.hip: one stage (HMOE_STAGE_W13 / _W2 / _COMBINE) of the decode path
 hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
-                         uint16_t* y, void* scratch, hipStream_t s);
+                         uint16_t* y, void* scratch, int stage, hipStream_t s);
 
-// prefill.hip
+// prefill.hip: one stage (HMOE_STAGE_W13 / _W2 / _COMBINE) of the prefill path
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
-                          uint16_t* y, void* scratch, hipStream_t s);
+                          uint16_t* y, void* scratch, int stage, hipStream_t s);
 
 // dequant.hip
 hipError_t launch_dequant(const Layer& L, const hmoe_weights& W, int expert, int tensor,
                           float* out_f32, uint16_t* out_bf16, hipStream_t s);
 
 TierMask make_tier_mask(const Layer& L);
+
+bool plan_gemv(int K, GemvTiling* t);
 
 }  // namespace hmoe

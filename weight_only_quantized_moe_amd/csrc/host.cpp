@@ -13,10 +13,6 @@ struct hmoe_layer {
   hmoe::Layer L;
 };
 
-namespace hmoe {
-bool plan_gemv(int K, int out_rows, bool w13, int min_rows, GemvTiling* t);
-}
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -61,6 +57,7 @@ void plan_scratch(hmoe::Layer& L) {
   P.d_experts = take((size_t)L.max_distinct * 4);
   P.d_nslots = take((size_t)L.max_distinct * 4);
   P.d_slots = take((size_t)L.max_distinct * hmoe::kDecodeMaxM * 4);
+  P.d_recs = take((size_t)L.max_distinct * hmoe::kGroupRec * 4);
   P.h_dec = take(dec_slots * L.I * 4);
   P.o_dec = take(dec_slots * L.H * 4);
   for (int t = 0; t < 2; ++t) {
@@ -169,7 +166,9 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
   L.max_distinct = std::min(hmoe::kDecodeMaxM * L.k, L.E);
   L.cap[0] = tier_capacity(L.max_tokens, L.k, L.E4, L.block_m);
   L.cap[1] = tier_capacity(L.max_tokens, L.k, L.E3, L.block_m);
-  if (!hmoe::plan_gemv(L.H, L.I, true, 16, &L.w13) || !hmoe::plan_gemv(L.I, L.H, false, 32, &L.w2)) {
+  const bool tiled = hmoe::plan_gemv(L.H, &L.w13) && hmoe::plan_gemv(L.I, &L.w2) &&
+                     L.I % ((64 / L.w13.lr) * L.w13.ri) == 0 && L.H % ((64 / L.w2.lr) * L.w2.ri) == 0;
+  if (!tiled) {
     delete h;
     return fail(HMOE_ERR_UNSUPPORTED, "no decode GEMV tiling for H=" + std::to_string(d->hidden) +
                                           ", I=" + std::to_string(d->inter));
@@ -275,12 +274,14 @@ hmoe_status moe_topk_view(const hmoe_layer* layer, void* scratch, int32_t** topk
   return HMOE_OK;
 }
 
-hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weights,
-                               const uint16_t* x, const float* router_logits, int32_t M,
-                               uint16_t* y, void* scratch, size_t scratch_bytes,
-                               hipStream_t stream) {
+hmoe_status hybrid_moe_forward_stage(const hmoe_layer* layer, const hmoe_weights* weights,
+                                     const uint16_t* x, const float* router_logits, int32_t M,
+                                     uint16_t* y, void* scratch, size_t scratch_bytes,
+                                     int32_t stage, hipStream_t stream) {
   if (hmoe_status st = check_layer(layer)) return st;
   const hmoe::Layer& L = layer->L;
+  if (stage < HMOE_STAGE_ROUTE || stage > HMOE_STAGE_COMBINE)
+    return fail(HMOE_ERR_INVALID_ARG, "unknown stage");
   if (M < 0) return fail(HMOE_ERR_INVALID_ARG, "M < 0");
   if (M > L.max_tokens) return fail(HMOE_ERR_CAPACITY, "M exceeds max_tokens");
   if (hmoe_status st = check_weights(L, weights)) return st;
@@ -288,19 +289,35 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
   if (hmoe_status st = check_scratch(L, scratch, scratch_bytes)) return st;
   if (!x || !router_logits || !y || !aligned(x, 16) || !aligned(router_logits, 16) || !aligned(y, 16))
     return fail(HMOE_ERR_ALIGN, "x, router_logits and y must be non-NULL and 16-byte aligned");
+  const bool decode = M <= hmoe::kDecodeMaxM;
   hipError_t err;
-  if (M <= hmoe::kDecodeMaxM) {
-    err = hmoe::launch_route_group(L, router_logits, M, scratch, stream);
-    if (err != hipSuccess) return hip_fail(err, "route/group launch");
-    err = hmoe::launch_decode(L, *weights, x, M, y, scratch, stream);
-    if (err != hipSuccess) return hip_fail(err, "decode launch");
+  if (stage == HMOE_STAGE_ROUTE) {
+    if (decode) {
+      err = hmoe::launch_route_group(L, router_logits, M, scratch, stream);
+    } else {
+      char* b = static_cast<char*>(scratch);
+      int32_t* ids = reinterpret_cast<int32_t*>(b + L.plan.topk_ids);
+      err = hmoe::launch_route(router_logits, M, L.E, L.k, ids,
+                               reinterpret_cast<float*>(b + L.plan.topk_w), stream);
+      if (err == hipSuccess) err = hmoe::launch_align(L, ids, M, scratch, stream);
+    }
+  } else if (decode) {
+    err = hmoe::launch_decode(L, *weights, x, M, y, scratch, stage, stream);
   } else {
-    char* b = static_cast<char*>(scratch);
-    err = hmoe::launch_route(router_logits, M, L.E, L.k, reinterpret_cast<int32_t*>(b + L.plan.topk_ids),
-                             reinterpret_cast<float*>(b + L.plan.topk_w), stream);
-    if (err != hipSuccess) return hip_fail(err, "route launch");
-    err = hmoe::launch_prefill(L, *weights, x, M, y, scratch, stream);
-    if (err != hipSuccess) return hip_fail(err, "prefill launch");
+    err = hmoe::launch_prefill(L, *weights, x, M, y, scratch, stage, stream);
+  }
+  if (err != hipSuccess) return hip_fail(err, "kernel launch");
+  return HMOE_OK;
+}
+
+hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weights,
+                               const uint16_t* x, const float* router_logits, int32_t M,
+                               uint16_t* y, void* scratch, size_t scratch_bytes,
+                               hipStream_t stream) {
+  for (int32_t stage = HMOE_STAGE_ROUTE; stage <= HMOE_STAGE_COMBINE; ++stage) {
+    const hmoe_status st = hybrid_moe_forward_stage(layer, weights, x, router_logits, M, y, scratch,
+                                                    scratch_bytes, stage, stream);
+    if (st != HMOE_OK) return st;
   }
   return HMOE_OK;
 }

@@ -46,6 +46,8 @@ struct PrefillArgs {
   const int32_t* bexp[2];
   const int32_t* npad[2];
   int nblk0;   // block count of tier 0 in this launch (tier 1 blocks follow)
+  int nblk1;
+  int E4, E3;
   int hrow1;   // h row of tier 1's first block
   int I, H;
   uint16_t* h_out;     // W13: fp16 [cap0 + cap1, I]
@@ -77,8 +79,11 @@ __global__ __launch_bounds__(kPfThreads) void grouped_gemm_kernel(PrefillArgs a)
   const int by = blockIdx.x;
   const int tier = by < a.nblk0 ? 0 : 1;
   const int b = tier ? by - a.nblk0 : by;
-  if (b * BM >= a.npad[tier][0]) return;
+  // npad and the block table come from the align stage; clamp to this launch's grid
+  // and the tier's expert count so stale scratch cannot index out of range
+  if (b * BM >= a.npad[tier][0] || b >= (tier ? a.nblk1 : a.nblk0)) return;
   const int loc = a.bexp[tier][b];
+  if ((unsigned)loc >= (unsigned)(tier ? a.E3 : a.E4)) return;
   const bool nf3 = tier == HMOE_TIER_NF3;
   const bool mx = !nf3 && a.kept_fmt == HMOE_KEPT_MXFP4;
   const int n0 = blockIdx.y * kBN;
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(kPfThreads) void grouped_gemm_kernel(PrefillArgs a)
       uint4 v = make_uint4(0, 0, 0, 0);
       if (W13) {
         const int slot = bslots[m];
-        if (slot < a.nslot)
+        if ((unsigned)slot < (unsigned)a.nslot)
           v = *reinterpret_cast<const uint4*>(a.act + (size_t)(slot / a.k) * a.K + k0 + 8 * ch);
       } else {
         v = *reinterpret_cast<const uint4*>(a.act + (hbase + m) * a.K + k0 + 8 * ch);
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(kPfThreads) void grouped_gemm_kernel(PrefillArgs a)
         a.h_out[(hbase + m) * a.I + n] = (uint16_t)(pack_f16(h, 0.0f) & 0xFFFFu);
       } else {
         const int slot = bslots[m];
-        if (slot < a.nslot) a.o_out[(size_t)slot * a.H + n] = acc[mt][0][r] * g * a.topk_w[slot];
+        if ((unsigned)slot < (unsigned)a.nslot) a.o_out[(size_t)slot * a.H + n] = acc[mt][0][r] * g * a.topk_w[slot];
       }
     }
   }
@@ -289,18 +294,16 @@ static GemmFn pick_gemm(int bm) {
 }
 
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
-                          uint16_t* y, void* scratch, hipStream_t s) {
+                          uint16_t* y, void* scratch, int stage, hipStream_t s) {
   char* base = static_cast<char*>(scratch);
   const ScratchPlan& P = L.plan;
-  int32_t* ids = reinterpret_cast<int32_t*>(base + P.topk_ids);
   float* w = reinterpret_cast<float*>(base + P.topk_w);
-  hipError_t err = launch_align(L, ids, M, scratch, s);
-  if (err != hipSuccess) return err;
-
   PrefillArgs a{};
   a.kept_fmt = L.kept_format;
   a.k = L.k;
   a.nslot = M * L.k;
+  a.E4 = L.E4;
+  a.E3 = L.E3;
   for (int t = 0; t < 2; ++t) {
     a.slots[t] = reinterpret_cast<const int32_t*>(base + P.a_slots[t]);
     a.bexp[t] = reinterpret_cast<const int32_t*>(base + P.a_bexp[t]);
@@ -311,15 +314,15 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
   const int ns = M * L.k;
   const int cap0 = ns + (L.E4 < ns ? L.E4 : ns) * (bm - 1);
   const int cap1 = ns + (L.E3 < ns ? L.E3 : ns) * (bm - 1);
-  const int nblk0 = L.E4 > 0 ? (cap0 + bm - 1) / bm : 0;
-  const int nblk1 = L.E3 > 0 ? (cap1 + bm - 1) / bm : 0;
-  a.nblk0 = nblk0;
+  a.nblk0 = L.E4 > 0 ? (cap0 + bm - 1) / bm : 0;
+  a.nblk1 = L.E3 > 0 ? (cap1 + bm - 1) / bm : 0;
   a.hrow1 = L.cap[0];
   a.I = L.I;
   a.H = L.H;
   uint16_t* h = reinterpret_cast<uint16_t*>(base + P.h_pre);
   float* o = reinterpret_cast<float*>(base + P.o_pre);
-  if (nblk0 + nblk1 > 0) {
+  const int nblk = a.nblk0 + a.nblk1;
+  if (stage == HMOE_STAGE_W13) {
     PrefillArgs b = a;
     b.kq = W.kept_w13_q; b.ks = W.kept_w13_s; b.kg = W.kept_w13_g;
     b.nq = W.nf3_w13_q; b.ns = W.nf3_w13_s;
@@ -329,10 +332,10 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     b.h_out = h;
     GemmFn fn = pick_gemm<true>(bm);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(nblk0 + nblk1, L.I / kBN), dim3(kPfThreads), 0, s, b);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
+    hipLaunchKernelGGL(fn, dim3(nblk, L.I / kBN), dim3(kPfThreads), 0, s, b);
+    return hipGetLastError();
+  }
+  if (stage == HMOE_STAGE_W2) {
     PrefillArgs c = a;
     c.kq = W.kept_w2_q; c.ks = W.kept_w2_s; c.kg = W.kept_w2_g;
     c.nq = W.nf3_w2_q; c.ns = W.nf3_w2_s;
@@ -341,16 +344,18 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     c.act = h;
     c.o_out = o;
     c.topk_w = w;
-    GemmFn fn2 = pick_gemm<false>(bm);
-    if (!fn2) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn2, dim3(nblk0 + nblk1, L.H / kBN), dim3(kPfThreads), 0, s, c);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    GemmFn fn = pick_gemm<false>(bm);
+    if (!fn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(nblk, L.H / kBN), dim3(kPfThreads), 0, s, c);
+    return hipGetLastError();
   }
-  const size_t n = (size_t)M * L.H;
-  hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, o,
-                     M, L.k, L.H, y);
-  return hipGetLastError();
+  if (stage == HMOE_STAGE_COMBINE) {
+    const size_t n = (size_t)M * L.H;
+    hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       o, M, L.k, L.H, y);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace hmoe

@@ -11,6 +11,18 @@ namespace hmoe {
 
 constexpr int kRouteWaves = 4;  // tokens per block of the general route kernel
 
+// One argmax butterfly step on (value, id): keep the larger value, ties to the lower
+// id (a total order, so every lane of the wave ends with the same winner).
+template <int B>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+  const float ov = xlane<B>(bv);
+  const int oi = xlane_i<B>(bi);
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
 // Top-k of one token's logits row by one wave. Experts rank by logit, descending,
 // ties to the lower id. Lane j < k ends with the j-th selection in (sel_v, sel_id).
 // Weights: softmax over the selected logits, in fp64, rounded once to fp32.
@@ -40,26 +52,27 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
         bi = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    argmax_step<32>(bv, bi);
+    argmax_step<16>(bv, bi);
+    argmax_step<8>(bv, bi);
+    argmax_step<4>(bv, bi);
+    argmax_step<2>(bv, bi);
+    argmax_step<1>(bv, bi);
     if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     if (lane == j) {
       sel_v = bv;
       sel_id = bi;
     }
   }
-  const float v0 = __shfl(sel_v, 0);
+  const float v0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(sel_v), 0));
   const double ex = (lane < k) ? exp((double)sel_v - (double)v0) : 0.0;
   double sum = ex;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  sum += xlane_d<32>(sum);
+  sum += xlane_d<16>(sum);
+  sum += xlane_d<8>(sum);
+  sum += xlane_d<4>(sum);
+  sum += xlane_d<2>(sum);
+  sum += xlane_d<1>(sum);
   if (lane < k) {
     ids_out[lane] = sel_id;
     w_out[lane] = (float)(ex / sum);
@@ -76,14 +89,12 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
   route_token(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
 }
 
-// Tier of expert e and its position in its tier's ascending-id storage.
-__device__ __forceinline__ int32_t tier_code(const TierMask& m, int e) {
+// Number of NF3-tier experts with id below 64 * chunk (the mask holds one bit per
+// expert, two words per 64-expert chunk).
+__device__ __forceinline__ int nf3_below_chunk(const TierMask& m, int chunk) {
   int below = 0;
-  const int wd = e >> 5;
-  for (int i = 0; i < wd; ++i) below += __popc(m.w[i]);
-  below += __popc(m.w[wd] & ((1u << (e & 31)) - 1u));
-  const bool nf3 = (m.w[wd] >> (e & 31)) & 1u;
-  return nf3 ? ((1 << 16) | below) : (e - below);
+  for (int i = 0; i < 2 * chunk; ++i) below += __popc(m.w[i]);
+  return below;
 }
 
 struct RouteGroupArgs {
@@ -96,22 +107,39 @@ struct RouteGroupArgs {
   int32_t* experts;    // [max_distinct]
   int32_t* nslots;     // [max_distinct]
   int32_t* slots;      // [max_distinct, 8]
+  int32_t* recs;       // [max_distinct, 16]: e, tier code, n, 0, slots[8], 0 x 4
 };
 
 constexpr int kGroupThreads = kDecodeMaxM * kWave;  // one wave per decode token
+constexpr int kGroupWaves = kDecodeMaxM;
 
 __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupArgs a, TierMask tm) {
   __shared__ int32_t s_ids[kDecodeMaxM * kMaxTopK];
   __shared__ uint32_t s_mask[kMaxExperts][4];   // slot bit masks (M * k <= 128 slots)
   __shared__ int32_t s_order[kMaxExperts];      // (tier, local) position -> expert or -1
+  __shared__ int32_t s_pos[kMaxExperts];        // expert -> (tier, local) position
+  __shared__ int32_t s_d[kMaxExperts];          // expert -> group index
+  __shared__ int32_t s_tc[kMaxExperts];         // expert -> tier code
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
   if (wave < a.M)
     route_token(a.logits + (size_t)wave * a.E, a.E, a.k, lane, a.ids + wave * a.k,
                 a.w + wave * a.k, s_ids + wave * a.k);
-  for (int e = threadIdx.x; e < a.E; e += kGroupThreads) {
-    a.expert_tier[e] = tier_code(tm, e);
-    s_mask[e][0] = s_mask[e][1] = s_mask[e][2] = s_mask[e][3] = 0u;
+  // tier map: one wave per 64-expert chunk, ranks by ballot
+  for (int chunk = wave; chunk * kWave < a.E; chunk += kGroupWaves) {
+    const int e = chunk * kWave + lane;
+    const bool in = e < a.E;
+    const bool nf3 = in && ((tm.w[e >> 5] >> (e & 31)) & 1u);
+    const uint64_t b = __ballot(nf3);
+    const int nf3_below = nf3_below_chunk(tm, chunk) + __popcll(b & lt);
+    if (in) {
+      const int32_t tc = nf3 ? ((1 << 16) | nf3_below) : (e - nf3_below);
+      a.expert_tier[e] = tc;
+      s_tc[e] = tc;
+      s_pos[e] = nf3 ? a.E4 + nf3_below : e - nf3_below;
+      s_mask[e][0] = s_mask[e][1] = s_mask[e][2] = s_mask[e][3] = 0u;
+    }
   }
   __syncthreads();
   const int nslot = a.M * a.k;
@@ -121,10 +149,8 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
   }
   __syncthreads();
   for (int e = threadIdx.x; e < a.E; e += kGroupThreads) {
-    const int32_t tc = tier_code(tm, e);
-    const int pos = (tc >> 16) ? a.E4 + (tc & 0xFFFF) : tc;
     const bool touched = (s_mask[e][0] | s_mask[e][1] | s_mask[e][2] | s_mask[e][3]) != 0u;
-    s_order[pos] = touched ? e : -1;
+    s_order[s_pos[e]] = touched ? e : -1;
   }
   __syncthreads();
   if (wave == 0) {
@@ -135,32 +161,38 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
       const int e = (pos < a.E) ? s_order[pos] : -1;
       const bool f = e >= 0;
       const uint64_t b = __ballot(f);
-      const int d = running + __popcll(b & ((1ull << lane) - 1ull));
       if (f) {
+        const int d = running + __popcll(b & lt);
+        s_d[e] = d;
         a.experts[d] = e;
-        int n = 0;
-        for (int wd = 0; wd < 4; ++wd) {
-          uint32_t m = s_mask[e][wd];
-          while (m) {
-            const int bit = __ffs(m) - 1;
-            m &= m - 1u;
-            if (n < kDecodeMaxM) a.slots[d * kDecodeMaxM + n] = wd * 32 + bit;
-            ++n;
-          }
-        }
+        const int n = __popc(s_mask[e][0]) + __popc(s_mask[e][1]) + __popc(s_mask[e][2]) +
+                      __popc(s_mask[e][3]);
         a.nslots[d] = n < kDecodeMaxM ? n : kDecodeMaxM;
+        int4* rec = reinterpret_cast<int4*>(a.recs + d * kGroupRec);
+        rec[0] = make_int4(e, s_tc[e], n < kDecodeMaxM ? n : kDecodeMaxM, 0);
+        rec[3] = make_int4(0, 0, 0, 0);
       }
       const int cnt = __popcll(b);
-      if (base + kWave <= a.E4) {
-        kept_distinct += cnt;
-      } else if (base < a.E4) {
-        kept_distinct += __popcll(b & ((1ull << (a.E4 - base)) - 1ull));
-      }
+      if (base + kWave <= a.E4) kept_distinct += cnt;
+      else if (base < a.E4) kept_distinct += __popcll(b & ((1ull << (a.E4 - base)) - 1ull));
       running += cnt;
     }
     if (lane == 0) {
       a.counts[0] = running;
       a.counts[1] = kept_distinct;
+    }
+  }
+  __syncthreads();
+  // each slot lands at its rank among its expert's slots (ascending slot order)
+  for (int s = threadIdx.x; s < nslot; s += kGroupThreads) {
+    const int e = s_ids[s];
+    if ((unsigned)e >= (unsigned)a.E) continue;
+    int rank = 0;
+    for (int wd = 0; wd < (s >> 5); ++wd) rank += __popc(s_mask[e][wd]);
+    rank += __popc(s_mask[e][s >> 5] & ((1u << (s & 31)) - 1u));
+    if (rank < kDecodeMaxM) {
+      a.slots[s_d[e] * kDecodeMaxM + rank] = s;
+      a.recs[s_d[e] * kGroupRec + 4 + rank] = s;
     }
   }
 }
@@ -190,6 +222,7 @@ hipError_t launch_route_group(const Layer& L, const float* logits, int M, void* 
   a.experts = reinterpret_cast<int32_t*>(base + L.plan.d_experts);
   a.nslots = reinterpret_cast<int32_t*>(base + L.plan.d_nslots);
   a.slots = reinterpret_cast<int32_t*>(base + L.plan.d_slots);
+  a.recs = reinterpret_cast<int32_t*>(base + L.plan.d_recs);
   hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, make_tier_mask(L));
   return hipGetLastError();
 }
