@@ -156,13 +156,18 @@ typedef struct hmoe_align_view {
  *               (tier, tier-local id); first counts[0] entries defined
  *   num_slots   int32 [max_distinct]: number of slots routed to each
  *   slots       int32 [max_distinct, 8]: those slots, ascending
- *   expert_tier int32 [E]: (tier << 16) | tier-local id of every expert */
+ *   expert_tier int32 [E]: (tier << 16) | tier-local id of every expert
+ *   passes      int32 [M * k, 4]: one record per slot, (slot, (tier << 16) | tier-local
+ *               id, token, expert), grouped by expert in the order of `experts`,
+ *               ascending slot within an expert; the decode GEMVs split their work
+ *               over these records */
 typedef struct hmoe_decode_view {
     int32_t* counts;
     int32_t* experts;
     int32_t* num_slots;
     int32_t* slots;
     int32_t* expert_tier;
+    int32_t* passes;
     int32_t max_distinct;
 } hmoe_decode_view;
 

@@ -140,6 +140,10 @@ def test_decode_grouping_bit_exact(hm, M):
     assert np.array_equal(et >> 16, tier) and np.array_equal(et & 0xFFFF, local)
     tids, tw = hm.moe_topk_view(layer, scratch, M)
     assert np.array_equal(tids.cpu().numpy(), ids)
+    # pass records: every slot once, grouped by expert in group order, slots ascending
+    passes = v["passes"].cpu().numpy()[: M * w.top_k]
+    want = [(s, (t << 16) | l, s // w.top_k, e) for (e, t, l, sl) in groups for s in sl]
+    assert [tuple(int(c) for c in r) for r in passes] == want
 
 
 # ---------------------------------------------------------------- align

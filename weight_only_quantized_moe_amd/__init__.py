@@ -62,7 +62,8 @@ class AlignView(Structure):
 
 class DecodeView(Structure):
     _fields_ = [("counts", c_void_p), ("experts", c_void_p), ("num_slots", c_void_p),
-                ("slots", c_void_p), ("expert_tier", c_void_p), ("max_distinct", c_int32)]
+                ("slots", c_void_p), ("expert_tier", c_void_p), ("passes", c_void_p),
+                ("max_distinct", c_int32)]
 
 
 _lib = None
@@ -214,14 +215,18 @@ def moe_decode_view(layer: Layer, scratch) -> dict:
     import torch
     v = DecodeView()
     _check(load_library().moe_decode_view(layer.handle, _ptr(scratch), byref(v)))
-    E = moe_layer_query(layer)["num_experts"]
+    info = moe_layer_query(layer)
+    E, k = info["num_experts"], info["top_k"]
     D = v.max_distinct
+    n_pass = DECODE_MAX_M * k
     return {
         "counts": _scratch_view(scratch, v.counts, 2, torch.int32),
         "experts": _scratch_view(scratch, v.experts, D, torch.int32),
         "num_slots": _scratch_view(scratch, v.num_slots, D, torch.int32),
         "slots": _scratch_view(scratch, v.slots, D * DECODE_MAX_M, torch.int32).view(D, DECODE_MAX_M),
         "expert_tier": _scratch_view(scratch, v.expert_tier, E, torch.int32),
+        # pass records of the first M * k slots of the last decode forward
+        "passes": _scratch_view(scratch, v.passes, n_pass * 4, torch.int32).view(n_pass, 4),
     }
 
 

@@ -1,31 +1,32 @@
 // Decode path (M <= 8): after routing and grouping, a GEMV over the packed W13 of
-// every distinct touched expert with a fused SwiGLU, a GEMV over their packed W2,
-// and the deterministic top-k weighted combine into y. Both tiers run in the same
-// launches from one routing result (local-inference-lab/vllm PR #92, "How it
-// works": launches sharing one route geometry and one top-k sum; M <= 8 addressed
-// directly by the top-k result).
+// every touched expert with a fused SwiGLU, a GEMV over their packed W2, and the
+// deterministic top-k weighted combine into y. Both tiers run in the same launches
+// from one routing result (local-inference-lab/vllm PR #92, "How it works":
+// launches sharing one route geometry and one top-k sum; M <= 8 addressed directly
+// by the top-k result).
 //
-// Work split: the rows of all touched experts form one flat range (W13: pairs of a
-// gate row i and its up row I + i; W2: rows n). It is cut into chunks of P * RI rows
-// (or pairs) and every wave of a persistent grid takes one contiguous, balanced run
-// of chunks, so each wave streams long stretches of one or two experts and reloads
-// its activations only when the expert changes. Inside a wave, LR lanes share a row
-// and each lane owns KU units of 32 K-elements (unit u = c + LR*j), so one load
+// Work split: every (token, top-k) slot is one pass over its expert's rows (W13:
+// pairs of a gate row i and its up row I + i; W2: rows n). The routing kernel lists
+// the passes grouped by expert, so a token pair sharing an expert streams the same
+// rows back to back (the second time from cache). Passes are cut into chunks of
+// P * RI rows (or pairs); the M * k * chunks-per-pass units form one flat range and
+// every wave of a persistent grid takes an equal contiguous run of it, so the work
+// is balanced whatever the expert multiplicities are, and a wave's first load (its
+// pass record) depends on nothing but its position. Inside a wave, LR lanes share a
+// row and each lane owns KU units of 32 K-elements (unit u = c + LR*j), so one load
 // instruction reads LR consecutive 16-byte (FP4) or 12-byte (NF3) units of each of
-// P = 64/LR rows. The lane's activations sit in
-// registers as 16-bit pairs and meet the decoded weights in v_dot2_f32_*; per-row
-// sums are finished by a transposing reduction across the LR lanes. A wave serves
-// one token per pass over its range; an expert with several tokens re-streams the
-// range (from cache) once per token, which keeps the activations, two chunks of
-// weights in flight, and the decoded values within the register budget.
+// P = 64/LR rows. The lane's activations sit in registers as 16-bit pairs and meet
+// the decoded weights in v_dot2_f32_*; per-row sums are finished by a transposing
+// reduction across the LR lanes. The next chunk's weights are in flight while the
+// current one is computed.
 //
 // Precision: W13 runs on bf16 pairs (x is bf16; E2M1 is exact in bf16; the NVFP4
 // E4M3 block scale multiplies each 16-block's fp32 partial; MXFP4's power-of-two
 // scale is folded into the conversion; NF3 levels come from a scaled table, see
 // kNF3TableScaleBf16, with the fp16 group scale on the fp32 partial). h leaves W13
-// in fp32. W2 runs on fp16 pairs: each slot's h row is scaled by a power of two so
-// its largest magnitude lands in [2^14, 2^15); E2M1 is exact in fp16 and every block
-// or group scale multiplies an fp32 partial.
+// in fp32. W2 runs on fp16 pairs: each pass stages its slot's h row in LDS scaled by
+// a power of two that puts the row's largest magnitude in [2^14, 2^15); E2M1 is
+// exact in fp16 and every block or group scale multiplies an fp32 partial.
 #include <type_traits>
 
 #include "device_common.h"
@@ -47,11 +48,9 @@ struct GemvArgs {
   int out_units;     // W13: I (row pairs per expert); W2: H (rows per expert)
   const uint16_t* act_bf16;  // W13: x bf16 [M, K]
   const float* act_f32;      // W2: h fp32 [slots, K]
-  int k;                     // top-k (x row of slot s is s / k)
-  const int32_t* counts;
-  const int32_t* recs;   // group records [bound, kGroupRec]
-  int bound;              // distinct experts at most (min(M*k, E))
-  int E, E4, E3, nslot;   // range checks of what the grouping left in scratch
+  const int4* pass;          // pass records [npass]: slot, tier code, token, expert
+  int npass;                 // M * k
+  int M, E, E4, E3;          // range checks of the records left in scratch
   int I;
   float* h_out;  // W13: fp32 [slots, I]
   float* o_out;  // W2: fp32 [slots, H]
@@ -196,37 +195,26 @@ struct RowDot {
   }
 };
 
-// Group d's record (one 48-byte load): tier, tier-local id and validated slot count
-// (0 when the grouping in scratch is stale or out of range). The slots themselves are
-// re-read per pass (slot_of): a register array indexed by the pass number would be
-// placed in private memory.
-struct ExpertInfo {
+// One pass: the slot it serves, the x row (token) it reads and its expert's tier
+// and tier-local index; ok is false for a record that is out of range (stale
+// scratch), which the pass then skips.
+struct PassInfo {
+  bool ok;
   bool nf3;
   int loc;
-  int n;
-  int d;
+  int slot;
+  int token;
 };
 
-__device__ __forceinline__ ExpertInfo expert_info(const GemvArgs& a, int d) {
-  const int4* rp = reinterpret_cast<const int4*>(a.recs + d * kGroupRec);
-  const int4 r0 = rp[0], r1 = rp[1], r2 = rp[2];
-  const int sl[kDecodeMaxM] = {r1.x, r1.y, r1.z, r1.w, r2.x, r2.y, r2.z, r2.w};
-  ExpertInfo r;
-  r.d = d;
-  r.nf3 = (r0.y >> 16) != 0;
-  r.loc = r0.y & 0xFFFF;
-  int n = min(r0.z, kDecodeMaxM);
-  if ((unsigned)r0.x >= (unsigned)a.E || r.loc >= (r.nf3 ? a.E3 : a.E4)) n = 0;
-#pragma unroll
-  for (int i = 0; i < kDecodeMaxM; ++i)
-    if (i < n && (unsigned)sl[i] >= (unsigned)a.nslot) n = 0;
-  r.n = n;
-  return r;
-}
-
-// slot of pass i (< ex.n, validated by expert_info)
-__device__ __forceinline__ int slot_of(const GemvArgs& a, const ExpertInfo& ex, int i) {
-  return a.recs[ex.d * kGroupRec + 4 + i];
+__device__ __forceinline__ PassInfo pass_info(const GemvArgs& a, int4 r) {
+  PassInfo p;
+  p.slot = r.x;
+  p.nf3 = (r.y >> 16) != 0;
+  p.loc = r.y & 0xFFFF;
+  p.token = r.z;
+  p.ok = (unsigned)r.x < (unsigned)a.npass && (unsigned)r.z < (unsigned)a.M &&
+         (unsigned)r.w < (unsigned)a.E && p.loc < (p.nf3 ? a.E3 : a.E4);
+  return p;
 }
 
 // Weight formats of one segment; the dispatch happens once per expert segment so
@@ -279,36 +267,45 @@ __device__ __forceinline__ void row_dot(const uint4 (&q)[KU], const uint32_t (&s
   else RowDot<LR, KU, NT, F16>::mxfp4(q, sc, x, acc);
 }
 
-// Calls f with the segment's format as a compile-time constant.
+// Calls f with the pass's weight format as a compile-time constant.
 template <typename F>
-__device__ __forceinline__ void with_format(const GemvArgs& a, const ExpertInfo& ex, F&& f) {
-  if (ex.nf3) f(std::integral_constant<int, kFmtNf3>{});
+__device__ __forceinline__ void with_format(const GemvArgs& a, const PassInfo& pi, F&& f) {
+  if (pi.nf3) f(std::integral_constant<int, kFmtNf3>{});
   else if (a.kept_fmt == HMOE_KEPT_NVFP4) f(std::integral_constant<int, kFmtNvfp4>{});
   else f(std::integral_constant<int, kFmtMxfp4>{});
+}
+
+// Position of this wave's run in the flat range of npass * per units.
+struct WaveRange {
+  int begin, end;
+};
+
+__device__ __forceinline__ WaveRange wave_range(int total) {
+  const int nw = gridDim.x * kGemvWaves;
+  // wave-uniform (scalar) from here on: the range, the pass, its tier and slot
+  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return {(int)((long)gw * total / nw), (int)((long)(gw + 1) * total / nw)};
 }
 
 // ---------------------------------------------------------------------------
 // W13 + SwiGLU
 // ---------------------------------------------------------------------------
 
-// x units of up to NT tokens (bf16 pairs) for this lane
-template <int LR, int KU, int NT>
-__device__ __forceinline__ void load_x(const GemvArgs& a, const int (&slot)[NT], int c,
-                                       uint32_t (&x)[NT][KU][16]) {
+// x units of one token (bf16 pairs) for this lane
+template <int LR, int KU>
+__device__ __forceinline__ void load_x(const GemvArgs& a, int token, int c,
+                                       uint32_t (&x)[1][KU][16]) {
+  const uint16_t* row = a.act_bf16 + (size_t)token * a.K;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const uint16_t* row = a.act_bf16 + (size_t)(slot[t] / a.k) * a.K;
+  for (int j = 0; j < KU; ++j) {
+    const uint4* p = reinterpret_cast<const uint4*>(row + 32 * (c + LR * j));
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const uint4* p = reinterpret_cast<const uint4*>(row + 32 * (c + LR * j));
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 qv = p[v];
-        x[t][j][4 * v + 0] = qv.x;
-        x[t][j][4 * v + 1] = qv.y;
-        x[t][j][4 * v + 2] = qv.z;
-        x[t][j][4 * v + 3] = qv.w;
-      }
+    for (int v = 0; v < 4; ++v) {
+      const uint4 qv = p[v];
+      x[0][j][4 * v + 0] = qv.x;
+      x[0][j][4 * v + 1] = qv.y;
+      x[0][j][4 * v + 2] = qv.z;
+      x[0][j][4 * v + 3] = qv.w;
     }
   }
 }
@@ -335,86 +332,70 @@ __device__ __forceinline__ void w13_load(const GemvArgs& a, int loc, int i0, W13
   }
 }
 
-template <int LR, int KU, int RI, int NT, int FMT>
-__device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, const int (&slot)[NT],
-                                            float g, const uint32_t (&x)[NT][KU][16],
+template <int LR, int KU, int RI, int FMT>
+__device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, int slot, float g,
+                                            const uint32_t (&x)[1][KU][16],
                                             const uint32_t* lut_lane, const W13Buf<KU, RI>& b) {
   constexpr int P = kWave / LR;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % LR;
   const int rw = lane / LR;
-  float vg[RI * NT], vu[RI * NT];
+  float vg[RI], vu[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
-    float ag[NT], au[NT];
-    row_dot<LR, KU, NT, false, FMT>(b.qg[ri], b.sg[ri], lut_lane, x, ag);
-    row_dot<LR, KU, NT, false, FMT>(b.qu[ri], b.su[ri], lut_lane, x, au);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      vg[ri * NT + t] = ag[t];
-      vu[ri * NT + t] = au[t];
-    }
+    float ag[1], au[1];
+    row_dot<LR, KU, 1, false, FMT>(b.qg[ri], b.sg[ri], lut_lane, x, ag);
+    row_dot<LR, KU, 1, false, FMT>(b.qu[ri], b.su[ri], lut_lane, x, au);
+    vg[ri] = ag[0];
+    vu[ri] = au[0];
   }
-  constexpr int V = RI * NT;
-  const float gate = seg_reduce<V, LR>(vg) * g;
-  const float up = seg_reduce<V, LR>(vu) * g;
-  const int o = seg_index<V, LR>(c);
-  if ((c & (LR / V - 1)) == 0) {
-    const int ri = o / NT;
-    const int t = o - ri * NT;
-    a.h_out[(size_t)slot[t] * a.I + i0 + ri * P + rw] = silu(gate) * up;
-  }
+  const float gate = seg_reduce<RI, LR>(vg) * g;
+  const float up = seg_reduce<RI, LR>(vu) * g;
+  const int ri = seg_index<RI, LR>(c);
+  if ((c & (LR / RI - 1)) == 0)
+    a.h_out[(size_t)slot * a.I + i0 + ri * P + rw] = silu(gate) * up;
 }
 
-// Chunks [c0, end) of one expert (chunk `first` is its pair 0), once per token of
-// the group: the next chunk's weights are in flight while the current one is
-// computed. A holds chunk c0 on entry when a_loaded.
+// Chunks [c0, end) of one pass (chunk `first` is the expert's pair 0). A holds
+// chunk c0 on entry when a_loaded.
 template <int LR, int KU, int RI, int FMT>
-__device__ __forceinline__ void w13_segment(const GemvArgs& a, const ExpertInfo& ex, int c0,
-                                            int end, int first, float g,
-                                            const uint32_t* lut_lane, W13Buf<KU, RI>& A,
-                                            W13Buf<KU, RI>& B, bool a_loaded) {
+__device__ __forceinline__ void w13_pass(const GemvArgs& a, const PassInfo& pi, int c0, int end,
+                                         int first, float g, const uint32_t* lut_lane,
+                                         W13Buf<KU, RI>& A, W13Buf<KU, RI>& B, bool a_loaded) {
   constexpr int CH = (kWave / LR) * RI;
   const int c = (threadIdx.x & (kWave - 1)) % LR;
-  for (int p = 0; p < ex.n; ++p) {
-    const int slot[1] = {slot_of(a, ex, p)};
-    int cc = c0;
-    if (!(a_loaded && p == 0)) w13_load<LR, KU, RI, FMT>(a, ex.loc, (cc - first) * CH, A);
-    uint32_t x[1][KU][16];
-    load_x<LR, KU, 1>(a, slot, c, x);
-    while (cc < end) {
-      if (cc + 1 < end) w13_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, B);
-      w13_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, A);
-      if (++cc >= end) break;
-      if (cc + 1 < end) w13_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, A);
-      w13_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, B);
-      ++cc;
-    }
+  int cc = c0;
+  if (!a_loaded) w13_load<LR, KU, RI, FMT>(a, pi.loc, (cc - first) * CH, A);
+  uint32_t x[1][KU][16];
+  load_x<LR, KU>(a, pi.token, c, x);
+  while (cc < end) {
+    if (cc + 1 < end) w13_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, B);
+    w13_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
+    if (++cc >= end) break;
+    if (cc + 1 < end) w13_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, A);
+    w13_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
+    ++cc;
   }
 }
 
 template <int LR, int KU, int RI>
 __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
   __shared__ uint32_t lut[64 * kWave];  // [pair field][lane]: bf16 pair of scaled NF3 levels
-  constexpr int P = kWave / LR;
-  constexpr int CH = P * RI;  // pairs per chunk
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t* lut_lane = lut + lane;
-  const int nd = min(a.counts[0], a.bound);
-  const int per_expert = a.out_units / CH;
-  const int total = nd * per_expert;
-  const int nw = gridDim.x * kGemvWaves;
-  // wave-uniform (scalar) from here on: the range, the expert, its tier and slots
-  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c_begin = (int)((long)gw * total / nw), c_end = (int)((long)(gw + 1) * total / nw);
+  constexpr int CH = (kWave / LR) * RI;  // pairs per chunk
+  const uint32_t* lut_lane = lut + (threadIdx.x & (kWave - 1));
+  const int per = a.out_units / CH;      // chunks per pass
+  const WaveRange wr = wave_range(a.npass * per);
   // the first chunk's weights are requested before the table is built
   W13Buf<KU, RI> A, B;
-  ExpertInfo ex{};
-  if (c_begin < c_end) {
-    ex = expert_info(a, c_begin / per_expert);
-    if (ex.n > 0)
-      with_format(a, ex, [&](auto f) {
-        w13_load<LR, KU, RI, decltype(f)::value>(a, ex.loc, (c_begin % per_expert) * CH, A);
+  PassInfo pi{};
+  int4 r_next{};
+  if (wr.begin < wr.end) {
+    const int p = wr.begin / per;
+    pi = pass_info(a, a.pass[p]);
+    if (p + 1 < a.npass) r_next = a.pass[p + 1];
+    if (pi.ok)
+      with_format(a, pi, [&](auto f) {
+        w13_load<LR, KU, RI, decltype(f)::value>(a, pi.loc, (wr.begin - p * per) * CH, A);
       });
   }
   for (int i = threadIdx.x; i < 64 * kWave; i += kGemvThreads) {
@@ -422,21 +403,24 @@ __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
     lut[i] = pack_bf16(nf3_level(f & 7) * kNF3TableScaleBf16, nf3_level(f >> 3) * kNF3TableScaleBf16);
   }
   __syncthreads();
-  int ch = c_begin;
-  bool first_seg = true;
-  while (ch < c_end) {
-    const int d = ch / per_expert;
-    const int d_end = min(c_end, (d + 1) * per_expert);
-    if (!first_seg) ex = expert_info(a, d);
-    const float g = ex.nf3 ? 1.0f / kNF3TableScaleBf16
-                           : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[ex.loc] : 1.0f);
-    // one token per pass: a second token re-streams this range from cache
-    with_format(a, ex, [&](auto f) {
-      w13_segment<LR, KU, RI, decltype(f)::value>(a, ex, ch, d_end, d * per_expert, g, lut_lane,
-                                                  A, B, first_seg);
-    });
-    first_seg = false;
-    ch = d_end;
+  bool first = true;
+  for (int ch = wr.begin; ch < wr.end;) {
+    const int p = ch / per;
+    const int p_end = min(wr.end, (p + 1) * per);
+    if (!first) {
+      pi = pass_info(a, r_next);
+      if (p + 1 < a.npass) r_next = a.pass[p + 1];
+    }
+    if (pi.ok) {
+      const float g = pi.nf3 ? 1.0f / kNF3TableScaleBf16
+                             : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[pi.loc] : 1.0f);
+      with_format(a, pi, [&](auto f) {
+        w13_pass<LR, KU, RI, decltype(f)::value>(a, pi, ch, p_end, p * per, g, lut_lane, A, B,
+                                                 first);
+      });
+    }
+    first = false;
+    ch = p_end;
   }
 }
 
@@ -444,40 +428,53 @@ __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
 // W2
 // ---------------------------------------------------------------------------
 
-// h units of up to NT slots, scaled by 2^-e[t] (e from the slot's largest |h| over
-// the whole row; every LR-lane segment of the wave covers the full row) and rounded
-// to fp16 pairs
-template <int LR, int KU, int NT>
-__device__ __forceinline__ void load_h(const GemvArgs& a, const int (&slot)[NT], int c,
-                                       uint32_t (&x)[NT][KU][16], int (&e)[NT]) {
+// Stages the slot's h row in this wave's LDS region as fp16 pairs scaled by 2^-e (e
+// from the row's largest |h|, so the largest lands in [2^14, 2^15)), then reads this
+// lane's KU units into x. Returns e.
+template <int LR, int KU>
+__device__ __forceinline__ int stage_h(const GemvArgs& a, int slot, uint32_t* hs, int c,
+                                       uint32_t (&x)[1][KU][16]) {
+  constexpr int NF4 = 8 * LR * KU;          // float4s per row (K = 32 * LR * KU)
+  constexpr int PER = (NF4 + kWave - 1) / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float4* row = reinterpret_cast<const float4*>(a.act_f32 + (size_t)slot * a.K);
+  float4 v[PER];
+  float mx = 0.0f;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float* row = a.act_f32 + (size_t)slot[t] * a.K;
-    float mx = 0.0f;
+  for (int i = 0; i < PER; ++i) {
+    const int f = lane + kWave * i;
+    v[i] = (NF4 % kWave == 0 || f < NF4) ? row[f] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  }
+  mx = group_max<kWave>(mx);
+  const int ef = (int)((__float_as_uint(mx) >> 23) & 0xFF);
+  const int e = mx > 0.0f ? (ef == 0 ? -126 : ef - 127) - 14 : 0;
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const float4* p = reinterpret_cast<const float4*>(row + 32 * (c + LR * j));
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const float4 q = p[v];
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
-      }
-    }
-    mx = group_max<LR>(mx);
-    // scale so that max * 2^-e lands in [2^14, 2^15), inside fp16's range
-    const int ef = (int)((__float_as_uint(mx) >> 23) & 0xFF);
-    e[t] = mx > 0.0f ? (ef == 0 ? -126 : ef - 127) - 14 : 0;
-#pragma unroll
-    for (int j = 0; j < KU; ++j) {
-      const float4* p = reinterpret_cast<const float4*>(row + 32 * (c + LR * j));
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const float4 q = p[v];
-        x[t][j][2 * v] = pack_f16(__builtin_ldexpf(q.x, -e[t]), __builtin_ldexpf(q.y, -e[t]));
-        x[t][j][2 * v + 1] = pack_f16(__builtin_ldexpf(q.z, -e[t]), __builtin_ldexpf(q.w, -e[t]));
-      }
+  for (int i = 0; i < PER; ++i) {
+    const int f = lane + kWave * i;
+    if (NF4 % kWave == 0 || f < NF4) {
+      uint2 w;
+      w.x = pack_f16(__builtin_ldexpf(v[i].x, -e), __builtin_ldexpf(v[i].y, -e));
+      w.y = pack_f16(__builtin_ldexpf(v[i].z, -e), __builtin_ldexpf(v[i].w, -e));
+      *reinterpret_cast<uint2*>(hs + 2 * f) = w;
     }
   }
+  // LDS operations of one wave complete in order: the reads below see the writes
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < KU; ++j) {
+    const uint4* p = reinterpret_cast<const uint4*>(hs + 16 * (c + LR * j));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 t = p[q];
+      x[0][j][4 * q + 0] = t.x;
+      x[0][j][4 * q + 1] = t.y;
+      x[0][j][4 * q + 2] = t.z;
+      x[0][j][4 * q + 3] = t.w;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  return e;
 }
 
 template <int KU, int RI>
@@ -497,78 +494,68 @@ __device__ __forceinline__ void w2_load(const GemvArgs& a, int loc, int n0, W2Bu
     load_row<LR, KU, FMT>(a, (size_t)loc * a.rows + n0 + ri * P + rw, c, b.q[ri], b.sc[ri]);
 }
 
-template <int LR, int KU, int RI, int NT, int FMT>
-__device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, const int (&slot)[NT],
-                                           const float (&g)[NT], const uint32_t (&x)[NT][KU][16],
+template <int LR, int KU, int RI, int FMT>
+__device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, int slot, float g,
+                                           const uint32_t (&x)[1][KU][16],
                                            const uint32_t* lut_lane, const W2Buf<KU, RI>& b) {
   constexpr int P = kWave / LR;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % LR;
   const int rw = lane / LR;
-  float v[RI * NT];
+  float v[RI];
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
-    float acc[NT];
-    row_dot<LR, KU, NT, true, FMT>(b.q[ri], b.sc[ri], lut_lane, x, acc);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[ri * NT + t] = acc[t];
+    float acc[1];
+    row_dot<LR, KU, 1, true, FMT>(b.q[ri], b.sc[ri], lut_lane, x, acc);
+    v[ri] = acc[0];
   }
-  constexpr int V = RI * NT;
-  const float sum = seg_reduce<V, LR>(v);
-  const int o = seg_index<V, LR>(c);
-  if ((c & (LR / V - 1)) == 0) {
-    const int ri = o / NT;
-    const int t = o - ri * NT;
-    a.o_out[(size_t)slot[t] * a.rows + n0 + ri * P + rw] = sum * g[t];
-  }
+  const float sum = seg_reduce<RI, LR>(v);
+  const int ri = seg_index<RI, LR>(c);
+  if ((c & (LR / RI - 1)) == 0) a.o_out[(size_t)slot * a.rows + n0 + ri * P + rw] = sum * g;
 }
 
 template <int LR, int KU, int RI, int FMT>
-__device__ __forceinline__ void w2_segment(const GemvArgs& a, const ExpertInfo& ex, int c0,
-                                           int end, int first, float gt,
-                                           const uint32_t* lut_lane, W2Buf<KU, RI>& A,
-                                           W2Buf<KU, RI>& B, bool a_loaded) {
+__device__ __forceinline__ void w2_pass(const GemvArgs& a, const PassInfo& pi, int c0, int end,
+                                        int first, float gt, const uint32_t* lut_lane,
+                                        uint32_t* hs, W2Buf<KU, RI>& A, W2Buf<KU, RI>& B,
+                                        bool a_loaded) {
   constexpr int CH = (kWave / LR) * RI;
   const int c = (threadIdx.x & (kWave - 1)) % LR;
-  for (int p = 0; p < ex.n; ++p) {
-    const int slot[1] = {slot_of(a, ex, p)};
-    int cc = c0;
-    if (!(a_loaded && p == 0)) w2_load<LR, KU, RI, FMT>(a, ex.loc, (cc - first) * CH, A);
-    uint32_t x[1][KU][16];
-    int e[1];
-    load_h<LR, KU, 1>(a, slot, c, x, e);
-    const float g[1] = {__builtin_ldexpf(gt, e[0])};
-    while (cc < end) {
-      if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, B);
-      w2_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, A);
-      if (++cc >= end) break;
-      if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, ex.loc, (cc + 1 - first) * CH, A);
-      w2_compute<LR, KU, RI, 1, FMT>(a, (cc - first) * CH, slot, g, x, lut_lane, B);
-      ++cc;
-    }
+  int cc = c0;
+  if (!a_loaded) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc - first) * CH, A);
+  uint32_t x[1][KU][16];
+  const float g = __builtin_ldexpf(gt, stage_h<LR, KU>(a, pi.slot, hs, c, x));
+  while (cc < end) {
+    if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, B);
+    w2_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
+    if (++cc >= end) break;
+    if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, A);
+    w2_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
+    ++cc;
   }
 }
 
+// dynamic LDS: one staged h row (K fp16) per wave
 template <int LR, int KU, int RI>
 __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
   __shared__ uint32_t lut[64 * kWave];  // [pair field][lane]: fp16 pair of scaled NF3 levels
-  constexpr int P = kWave / LR;
-  constexpr int CH = P * RI;  // rows per chunk
-  const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t* lut_lane = lut + lane;
-  const int nd = min(a.counts[0], a.bound);
-  const int per_expert = a.out_units / CH;
-  const int total = nd * per_expert;
-  const int nw = gridDim.x * kGemvWaves;
-  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c_begin = (int)((long)gw * total / nw), c_end = (int)((long)(gw + 1) * total / nw);
+  extern __shared__ uint32_t h_stage[];
+  constexpr int CH = (kWave / LR) * RI;  // rows per chunk
+  constexpr int KD = 16 * LR * KU;        // dwords per staged row (K / 2)
+  const uint32_t* lut_lane = lut + (threadIdx.x & (kWave - 1));
+  uint32_t* hs = h_stage + KD * (threadIdx.x >> 6);
+  const int per = a.out_units / CH;
+  const WaveRange wr = wave_range(a.npass * per);
   W2Buf<KU, RI> A, B;
-  ExpertInfo ex{};
-  if (c_begin < c_end) {
-    ex = expert_info(a, c_begin / per_expert);
-    if (ex.n > 0)
-      with_format(a, ex, [&](auto f) {
-        w2_load<LR, KU, RI, decltype(f)::value>(a, ex.loc, (c_begin % per_expert) * CH, A);
+  PassInfo pi{};
+  int4 r_next{};
+  if (wr.begin < wr.end) {
+    const int p = wr.begin / per;
+    pi = pass_info(a, a.pass[p]);
+    if (p + 1 < a.npass) r_next = a.pass[p + 1];
+    if (pi.ok)
+      with_format(a, pi, [&](auto f) {
+        w2_load<LR, KU, RI, decltype(f)::value>(a, pi.loc, (wr.begin - p * per) * CH, A);
       });
   }
   for (int i = threadIdx.x; i < 64 * kWave; i += kGemvThreads) {
@@ -576,20 +563,24 @@ __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
     lut[i] = pack_f16(nf3_level(f & 7) * kNF3TableScaleF16, nf3_level(f >> 3) * kNF3TableScaleF16);
   }
   __syncthreads();
-  int ch = c_begin;
-  bool first_seg = true;
-  while (ch < c_end) {
-    const int d = ch / per_expert;
-    const int d_end = min(c_end, (d + 1) * per_expert);
-    if (!first_seg) ex = expert_info(a, d);
-    const float gt = ex.nf3 ? 1.0f / kNF3TableScaleF16
-                            : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[ex.loc] : 1.0f);
-    with_format(a, ex, [&](auto f) {
-      w2_segment<LR, KU, RI, decltype(f)::value>(a, ex, ch, d_end, d * per_expert, gt, lut_lane,
-                                                 A, B, first_seg);
-    });
-    first_seg = false;
-    ch = d_end;
+  bool first = true;
+  for (int ch = wr.begin; ch < wr.end;) {
+    const int p = ch / per;
+    const int p_end = min(wr.end, (p + 1) * per);
+    if (!first) {
+      pi = pass_info(a, r_next);
+      if (p + 1 < a.npass) r_next = a.pass[p + 1];
+    }
+    if (pi.ok) {
+      const float gt = pi.nf3 ? 1.0f / kNF3TableScaleF16
+                              : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[pi.loc] : 1.0f);
+      with_format(a, pi, [&](auto f) {
+        w2_pass<LR, KU, RI, decltype(f)::value>(a, pi, ch, p_end, p * per, gt, lut_lane, hs, A,
+                                                B, first);
+      });
+    }
+    first = false;
+    ch = p_end;
   }
 }
 
@@ -638,8 +629,8 @@ static GemvFn pick_gemv(const GemvTiling& t) {
 
 // Decode GEMV tiling over reduction length K: LR = the largest power of two up to 64
 // dividing the K/32 units, KU = units per lane, RI = rows (or row pairs) per lane per
-// chunk, bounded so the values a lane reduces (RI * 2 tokens per reduction) never
-// outnumber the lanes of its LR-lane segment.
+// chunk, at most half the lanes of an LR-lane segment (the transposing reduction
+// hands each row's sum to LR / RI lanes).
 bool plan_gemv(int K, GemvTiling* t) {
   const int U = K / 32;
   int lr = 1;
@@ -655,23 +646,27 @@ bool plan_gemv(int K, GemvTiling* t) {
   return true;
 }
 
-// blocks of one GEMV kernel resident per CU (occupancy query, cached per kernel)
-static int resident_blocks(GemvFn fn) {
-  static GemvFn fns[16] = {};
-  static int counts[16] = {};
-  for (int i = 0; i < 16; ++i) {
-    if (fns[i] == fn) return counts[i];
-    if (fns[i] == nullptr) {
+// blocks of one GEMV kernel resident per CU at the given dynamic LDS size (occupancy
+// query, cached)
+static int resident_blocks(GemvFn fn, size_t smem) {
+  struct Entry {
+    GemvFn fn;
+    size_t smem;
+    int n;
+  };
+  static Entry cache[32] = {};
+  for (int i = 0; i < 32; ++i) {
+    if (cache[i].fn == fn && cache[i].smem == smem) return cache[i].n;
+    if (cache[i].fn == nullptr) {
       int n = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
-                                                       kGemvThreads, 0) != hipSuccess || n < 1)
-        n = 2;
-      fns[i] = fn;
-      counts[i] = n;
+                                                       kGemvThreads, smem) != hipSuccess || n < 1)
+        n = 1;
+      cache[i] = {fn, smem, n};
       return n;
     }
   }
-  return 2;
+  return 1;
 }
 
 static int cu_count() {
@@ -689,27 +684,26 @@ static int cu_count() {
 
 hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
                          uint16_t* y, void* scratch, int stage, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
   char* base = static_cast<char*>(scratch);
   const ScratchPlan& P = L.plan;
   GemvArgs a{};
   a.kept_fmt = L.kept_format;
-  a.counts = reinterpret_cast<const int32_t*>(base + P.d_counts);
-  a.recs = reinterpret_cast<const int32_t*>(base + P.d_recs);
-  a.I = L.I;
+  a.pass = reinterpret_cast<const int4*>(base + P.d_pass);
+  a.npass = M * L.k;
+  a.M = M;
   a.E = L.E;
   a.E4 = L.E4;
   a.E3 = L.E3;
-  a.k = L.k;
-  a.nslot = M * L.k;
-  a.bound = (M * L.k < L.max_distinct) ? M * L.k : L.max_distinct;
+  a.I = L.I;
   float* h = reinterpret_cast<float*>(base + P.h_dec);
   float* o = reinterpret_cast<float*>(base + P.o_dec);
   // a persistent grid: as many blocks as fit on the GPU at once, never more waves
   // than chunks
-  auto grid_for = [&](GemvFn fn, const GemvTiling& t, int out_units) {
-    const long chunks = (long)a.bound * (out_units / ((64 / t.lr) * t.ri));
+  auto grid_for = [&](GemvFn fn, const GemvTiling& t, int out_units, size_t smem) {
+    const long chunks = (long)a.npass * (out_units / ((64 / t.lr) * t.ri));
     const long blocks = (chunks + kGemvWaves - 1) / kGemvWaves;
-    const long cap = (long)resident_blocks(fn) * cu_count();
+    const long cap = (long)resident_blocks(fn, smem) * cu_count();
     return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
   };
   if (stage == HMOE_STAGE_W13) {
@@ -721,7 +715,7 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
     b.h_out = h;
     GemvFn fn = pick_gemv<true>(L.w13);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(grid_for(fn, L.w13, L.I)), dim3(kGemvThreads), 0, s, b);
+    hipLaunchKernelGGL(fn, dim3(grid_for(fn, L.w13, L.I, 0)), dim3(kGemvThreads), 0, s, b);
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_W2) {
@@ -733,7 +727,8 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
     b.o_out = o;
     GemvFn fn = pick_gemv<false>(L.w2);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(grid_for(fn, L.w2, L.H)), dim3(kGemvThreads), 0, s, b);
+    const size_t smem = (size_t)kGemvWaves * L.I * 2;  // one fp16 h row per wave
+    hipLaunchKernelGGL(fn, dim3(grid_for(fn, L.w2, L.H, smem)), dim3(kGemvThreads), smem, s, b);
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_COMBINE) {

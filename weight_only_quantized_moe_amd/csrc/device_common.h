@@ -29,11 +29,19 @@ constexpr int kWave = 64;
 // an exact zero, scaled so that the ends are -1 and +1), as fp32 bit patterns in
 // ascending level order.
 // ---------------------------------------------------------------------------
-__device__ __constant__ static const uint32_t kNF3Bits[8] = {
+constexpr uint32_t kNF3Bits[8] = {
     0xBF800000u, 0xBF08F740u, 0xBE7CDB98u, 0x00000000u,
     0x3E3BBCD2u, 0x3EC394B6u, 0x3F1F7BFEu, 0x3F800000u};
 
-__device__ __forceinline__ float nf3_level(uint32_t q) { return __uint_as_float(kNF3Bits[q & 7]); }
+// level of code q (a select chain over immediates: an indexed table would be a
+// memory load)
+__device__ __forceinline__ float nf3_level(uint32_t q) {
+  q &= 7u;
+  uint32_t b = kNF3Bits[0];
+#pragma unroll
+  for (uint32_t i = 1; i < 8; ++i) b = (q == i) ? kNF3Bits[i] : b;
+  return __uint_as_float(b);
+}
 
 // Level tables inside the kernels hold level * c rounded to 16 bits, with c chosen
 // so that all eight products are close to representable: the largest relative

@@ -58,6 +58,7 @@ void plan_scratch(hmoe::Layer& L) {
   P.d_nslots = take((size_t)L.max_distinct * 4);
   P.d_slots = take((size_t)L.max_distinct * hmoe::kDecodeMaxM * 4);
   P.d_recs = take((size_t)L.max_distinct * hmoe::kGroupRec * 4);
+  P.d_pass = take(dec_slots * hmoe::kPassRec * 4);
   P.h_dec = take(dec_slots * L.I * 4);
   P.o_dec = take(dec_slots * L.H * 4);
   for (int t = 0; t < 2; ++t) {
@@ -261,6 +262,7 @@ hmoe_status moe_decode_view(const hmoe_layer* layer, void* scratch, hmoe_decode_
   out->num_slots = reinterpret_cast<int32_t*>(b + L.plan.d_nslots);
   out->slots = reinterpret_cast<int32_t*>(b + L.plan.d_slots);
   out->expert_tier = reinterpret_cast<int32_t*>(b + L.plan.expert_tier);
+  out->passes = reinterpret_cast<int32_t*>(b + L.plan.d_pass);
   out->max_distinct = L.max_distinct;
   return HMOE_OK;
 }

@@ -108,6 +108,7 @@ struct RouteGroupArgs {
   int32_t* nslots;     // [max_distinct]
   int32_t* slots;      // [max_distinct, 8]
   int32_t* recs;       // [max_distinct, 16]: e, tier code, n, 0, slots[8], 0 x 4
+  int32_t* pass;       // [M * k, 4]: slot, tier code, token, e (grouped by expert)
 };
 
 constexpr int kGroupThreads = kDecodeMaxM * kWave;  // one wave per decode token
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
   __shared__ int32_t s_pos[kMaxExperts];        // expert -> (tier, local) position
   __shared__ int32_t s_d[kMaxExperts];          // expert -> group index
   __shared__ int32_t s_tc[kMaxExperts];         // expert -> tier code
+  __shared__ int32_t s_poff[kMaxExperts];       // expert -> first pass record
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
@@ -154,19 +156,28 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
   }
   __syncthreads();
   if (wave == 0) {
-    int running = 0;
+    int running = 0, running_slots = 0;
     int kept_distinct = 0;
     for (int base = 0; base < a.E; base += kWave) {
       const int pos = base + lane;
       const int e = (pos < a.E) ? s_order[pos] : -1;
       const bool f = e >= 0;
       const uint64_t b = __ballot(f);
+      const int n = f ? __popc(s_mask[e][0]) + __popc(s_mask[e][1]) + __popc(s_mask[e][2]) +
+                            __popc(s_mask[e][3])
+                      : 0;
+      // inclusive scan of the slot counts over the wave: first pass record of each
+      int incl = n;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
       if (f) {
         const int d = running + __popcll(b & lt);
         s_d[e] = d;
+        s_poff[e] = running_slots + incl - n;
         a.experts[d] = e;
-        const int n = __popc(s_mask[e][0]) + __popc(s_mask[e][1]) + __popc(s_mask[e][2]) +
-                      __popc(s_mask[e][3]);
         a.nslots[d] = n < kDecodeMaxM ? n : kDecodeMaxM;
         int4* rec = reinterpret_cast<int4*>(a.recs + d * kGroupRec);
         rec[0] = make_int4(e, s_tc[e], n < kDecodeMaxM ? n : kDecodeMaxM, 0);
@@ -176,6 +187,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
       if (base + kWave <= a.E4) kept_distinct += cnt;
       else if (base < a.E4) kept_distinct += __popcll(b & ((1ull << (a.E4 - base)) - 1ull));
       running += cnt;
+      running_slots += __shfl(incl, kWave - 1);
     }
     if (lane == 0) {
       a.counts[0] = running;
@@ -194,6 +206,9 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
       a.slots[s_d[e] * kDecodeMaxM + rank] = s;
       a.recs[s_d[e] * kGroupRec + 4 + rank] = s;
     }
+    const int p = s_poff[e] + rank;
+    if (p < nslot)
+      reinterpret_cast<int4*>(a.pass)[p] = make_int4(s, s_tc[e], s / a.k, e);
   }
 }
 
@@ -223,6 +238,7 @@ hipError_t launch_route_group(const Layer& L, const float* logits, int M, void* 
   a.nslots = reinterpret_cast<int32_t*>(base + L.plan.d_nslots);
   a.slots = reinterpret_cast<int32_t*>(base + L.plan.d_slots);
   a.recs = reinterpret_cast<int32_t*>(base + L.plan.d_recs);
+  a.pass = reinterpret_cast<int32_t*>(base + L.plan.d_pass);
   hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, make_tier_mask(L));
   return hipGetLastError();
 }
