@@ -287,6 +287,24 @@ __device__ __forceinline__ WaveRange wave_range(int total) {
   return {(int)((long)gw * total / nw), (int)((long)(gw + 1) * total / nw)};
 }
 
+// Builds the per-lane NF3 pair table [64 pair fields][64 lanes]: entry f holds the
+// 16-bit pair (level(f & 7) * c, level(f >> 3) * c), bf16 or fp16. Thread t of the
+// 256 writes fields (t >> 6) + 4m, m = 0..15, of lane t & 63: its low code takes two
+// values and its high code is m >> 1, a constant once the loop is unrolled.
+template <bool F16>
+__device__ __forceinline__ void build_nf3_lut(uint32_t* lut, float c) {
+  static_assert(kGemvThreads == 256, "four waves build the table");
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float lo0 = nf3_level(w) * c, lo1 = nf3_level(w + 4) * c;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float hi = __uint_as_float(kNF3Bits[m >> 1]) * c;
+    const float lo = (m & 1) ? lo1 : lo0;
+    lut[(w + 4 * m) * kWave + lane] = F16 ? pack_f16(lo, hi) : pack_bf16(lo, hi);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // W13 + SwiGLU
 // ---------------------------------------------------------------------------
@@ -388,19 +406,20 @@ __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
   // the first chunk's weights are requested before the table is built
   W13Buf<KU, RI> A, B;
   PassInfo pi{};
-  int4 r_next{};
+  int4 r_first{}, r_next{};
   if (wr.begin < wr.end) {
     const int p = wr.begin / per;
-    pi = pass_info(a, a.pass[p]);
+    r_first = a.pass[p];
     if (p + 1 < a.npass) r_next = a.pass[p + 1];
+  }
+  build_nf3_lut<false>(lut, kNF3TableScaleBf16);
+  if (wr.begin < wr.end) {
+    const int p = wr.begin / per;
+    pi = pass_info(a, r_first);
     if (pi.ok)
       with_format(a, pi, [&](auto f) {
         w13_load<LR, KU, RI, decltype(f)::value>(a, pi.loc, (wr.begin - p * per) * CH, A);
       });
-  }
-  for (int i = threadIdx.x; i < 64 * kWave; i += kGemvThreads) {
-    const int f = i / kWave;
-    lut[i] = pack_bf16(nf3_level(f & 7) * kNF3TableScaleBf16, nf3_level(f >> 3) * kNF3TableScaleBf16);
   }
   __syncthreads();
   bool first = true;
@@ -548,19 +567,20 @@ __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
   const WaveRange wr = wave_range(a.npass * per);
   W2Buf<KU, RI> A, B;
   PassInfo pi{};
-  int4 r_next{};
+  int4 r_first{}, r_next{};
   if (wr.begin < wr.end) {
     const int p = wr.begin / per;
-    pi = pass_info(a, a.pass[p]);
+    r_first = a.pass[p];
     if (p + 1 < a.npass) r_next = a.pass[p + 1];
+  }
+  build_nf3_lut<true>(lut, kNF3TableScaleF16);
+  if (wr.begin < wr.end) {
+    const int p = wr.begin / per;
+    pi = pass_info(a, r_first);
     if (pi.ok)
       with_format(a, pi, [&](auto f) {
         w2_load<LR, KU, RI, decltype(f)::value>(a, pi.loc, (wr.begin - p * per) * CH, A);
       });
-  }
-  for (int i = threadIdx.x; i < 64 * kWave; i += kGemvThreads) {
-    const int f = i / kWave;
-    lut[i] = pack_f16(nf3_level(f & 7) * kNF3TableScaleF16, nf3_level(f >> 3) * kNF3TableScaleF16);
   }
   __syncthreads();
   bool first = true;

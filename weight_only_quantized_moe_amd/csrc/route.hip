@@ -23,18 +23,21 @@ __device__ __forceinline__ void argmax_step(float& bv, int& bi) {
   }
 }
 
-// Top-k of one token's logits row by one wave. Experts rank by logit, descending,
-// ties to the lower id. Lane j < k ends with the j-th selection in (sel_v, sel_id).
-// Weights: softmax over the selected logits, in fp64, rounded once to fp32.
+// Top-k of one token's logits row by one wave; each lane holds NV >= E / 64 logits
+// (lane + 64 i). Experts rank by logit, descending, ties to the lower id; each of the
+// k rounds takes every lane's best remaining logit and a butterfly argmax over the
+// wave. Lane j < k ends with the j-th selection in (sel_v, sel_id). Weights: softmax
+// over the selected logits, in fp64, rounded once to fp32.
+template <int NV>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
                                             int32_t* __restrict__ ids_out,
                                             float* __restrict__ w_out, int32_t* lds_ids) {
-  float v[16];
+  float v[NV];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = lane + kWave * i;
-    v[i] = (e < E) ? row[e] : -INFINITY;
-    if (v[i] != v[i]) v[i] = -INFINITY;  // NaN ranks below every number: a total order
+    const float t = (e < E) ? row[e] : -INFINITY;
+    v[i] = (t != t) ? -INFINITY : t;  // NaN ranks below every number: a total order
   }
   uint32_t taken = 0;
   float sel_v = 0.0f;
@@ -43,7 +46,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int e = lane + kWave * i;
       const bool ok = (e < E) && !((taken >> i) & 1u);
       // ids grow with i inside a lane, so a strict > keeps the lowest id on ties
@@ -80,13 +83,37 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   }
 }
 
+// route_token with NV = the smallest power of two covering E / 64 logits per lane
+__device__ __forceinline__ void route_token_any(const float* __restrict__ row, int E, int k,
+                                                int lane, int32_t* __restrict__ ids_out,
+                                                float* __restrict__ w_out, int32_t* lds_ids) {
+  if (E <= 64) route_token<1>(row, E, k, lane, ids_out, w_out, lds_ids);
+  else if (E <= 128) route_token<2>(row, E, k, lane, ids_out, w_out, lds_ids);
+  else if (E <= 256) route_token<4>(row, E, k, lane, ids_out, w_out, lds_ids);
+  else if (E <= 512) route_token<8>(row, E, k, lane, ids_out, w_out, lds_ids);
+  else route_token<16>(row, E, k, lane, ids_out, w_out, lds_ids);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then each row's total carried into the rows above (DPP row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const float* __restrict__ logits, int M, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ w) {
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
   if (t >= M) return;
-  route_token(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+  route_token_any(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k,
+                  nullptr);
 }
 
 // Number of NF3-tier experts with id below 64 * chunk (the mask holds one bit per
@@ -126,7 +153,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
   const int wave = threadIdx.x >> 6;
   const uint64_t lt = (1ull << lane) - 1ull;
   if (wave < a.M)
-    route_token(a.logits + (size_t)wave * a.E, a.E, a.k, lane, a.ids + wave * a.k,
+    route_token_any(a.logits + (size_t)wave * a.E, a.E, a.k, lane, a.ids + wave * a.k,
                 a.w + wave * a.k, s_ids + wave * a.k);
   // tier map: one wave per 64-expert chunk, ranks by ballot
   for (int chunk = wave; chunk * kWave < a.E; chunk += kGroupWaves) {
@@ -167,12 +194,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
                             __popc(s_mask[e][3])
                       : 0;
       // inclusive scan of the slot counts over the wave: first pass record of each
-      int incl = n;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
+      const int incl = wave_incl_scan(n);
       if (f) {
         const int d = running + __popcll(b & lt);
         s_d[e] = d;
@@ -187,7 +209,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
       if (base + kWave <= a.E4) kept_distinct += cnt;
       else if (base < a.E4) kept_distinct += __popcll(b & ((1ull << (a.E4 - base)) - 1ull));
       running += cnt;
-      running_slots += __shfl(incl, kWave - 1);
+      running_slots += __builtin_amdgcn_readlane(incl, kWave - 1);
     }
     if (lane == 0) {
       a.counts[0] = running;
