@@ -98,7 +98,7 @@ def pmc_traffic(kernel_key, src_hash, launches_bytes):
         return None
 
 
-def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None):
+def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=None):
     """Times `steps` graph replays of the forward at w.M; returns a result dict."""
     import numpy as np
     import torch
@@ -112,7 +112,9 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None):
         log(f"{w.name}: generated packed layer in {time.time() - t0:.1f}s")
     bm = packed["bit_map"]
     fmt = hm.KEPT_NVFP4 if packed["kept_format"] == "nvfp4" else hm.KEPT_MXFP4
-    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, 32)
+    if block_m is None:
+        block_m = 128 if w.M > hm.DECODE_MAX_M else 32
+    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, block_m)
     base = hm.DeviceWeights(packed)
     layer_bytes = base.nbytes()
     if copies is None:
@@ -167,7 +169,7 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None):
     # algorithmic work from the routing this batch produced
     eb = expert_bytes(packed)
     k, M = w.top_k, w.M
-    res = {"ms_per_step": ms_per_step, "stage_us": stage_us, "copies": copies,
+    res = {"ms_per_step": ms_per_step, "stage_us": stage_us, "copies": copies, "block_m": block_m,
            "layer_bytes_resident": layer_bytes, "desc": describe(w, packed)}
     io_bytes = M * w.H * 2 + M * w.E * 4 + M * w.H * 2        # x, logits, y
     if M <= hm.DECODE_MAX_M:
@@ -238,6 +240,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1,2,4 decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--block-m", type=int, default=None,
+                    help="prefill GEMM rows per expert block (16/32/64/128; default 128)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -256,7 +260,7 @@ def main():
     w = workload(args.workload, args.m)
     decode = w.M <= hm.DECODE_MAX_M
     log(f"measuring {w.name} (M={w.M}), {args.steps} steps after {args.warmup} warm-up")
-    r = measure(w, args.steps, args.warmup, args.copies)
+    r = measure(w, args.steps, args.warmup, args.copies, block_m=args.block_m)
     ms = r["ms_per_step"]
     out = {
         "metric": METRIC,
@@ -299,6 +303,7 @@ def main():
                            "avg_launch_us": r["stage_us"][1],
                            "traffic": pmc_traffic("prefill_w13_" + w.name, src, None)}
         out["config"]["touched_experts"] = r["touched_experts"]
+        out["config"]["block_m"] = r["block_m"]
     if decode and args.workload == "qwen_decode" and not args.no_sweep and args.m is None:
         sweep = []
         for m in (1, 2, 4):

@@ -85,6 +85,7 @@ def test_scratch_planner_covers_every_region():
     needed = ((q["cap_kept"] + q["cap_nf3"]) * I * 2      # prefill h (fp16)
               + M * k * H * 4                              # per-slot outputs (fp32)
               + 8 * k * H * 4 + 8 * k * I * 4              # decode intermediates (fp32)
+              + M * H * 2 + M * 4                          # prefill x as scaled fp16
               + (q["cap_kept"] + q["cap_nf3"]) * 4)        # sorted slots
     assert needed <= n < needed + 64 * 1024 + 16 * (q["cap_kept"] + q["cap_nf3"])
     small = hm.moe_layer_create(E, H, I, k, 8, hm.KEPT_NVFP4, [4] * 64 + [3] * 192, 32)

@@ -29,7 +29,7 @@ struct ScratchPlan {
   size_t h_dec = 0, o_dec = 0;
   size_t a_counts = 0;                     // int32 [E] slot counts per expert
   size_t a_slots[2] = {0, 0}, a_bexp[2] = {0, 0}, a_eoff[2] = {0, 0}, a_npad[2] = {0, 0};
-  size_t h_pre = 0, o_pre = 0;
+  size_t h_pre = 0, o_pre = 0, x16_pre = 0, xe_pre = 0;
   size_t total = 0;
 };
 

@@ -72,9 +72,13 @@ void plan_scratch(hmoe::Layer& L) {
   if (L.max_tokens > hmoe::kDecodeMaxM) {
     P.h_pre = take((size_t)(L.cap[0] + L.cap[1]) * L.I * 2);
     P.o_pre = take(mk * L.H * 4);
+    P.x16_pre = take((size_t)L.max_tokens * L.H * 2);
+    P.xe_pre = take((size_t)L.max_tokens * 4);
   } else {
     P.h_pre = take(0);
     P.o_pre = take(0);
+    P.x16_pre = take(0);
+    P.xe_pre = take(0);
   }
   P.total = off;
 }
@@ -167,6 +171,12 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
   L.max_distinct = std::min(hmoe::kDecodeMaxM * L.k, L.E);
   L.cap[0] = tier_capacity(L.max_tokens, L.k, L.E4, L.block_m);
   L.cap[1] = tier_capacity(L.max_tokens, L.k, L.E3, L.block_m);
+  // the prefill GEMMs put the expert blocks of both tiers on the grid's y axis
+  if ((long)(L.cap[0] + L.cap[1]) / L.block_m > 65535) {
+    delete h;
+    return fail(HMOE_ERR_UNSUPPORTED, "max_tokens * top_k / block_m too large (more than "
+                                      "65535 expert blocks): use a larger block_m");
+  }
   const bool tiled = hmoe::plan_gemv(L.H, &L.w13) && hmoe::plan_gemv(L.I, &L.w2) &&
                      L.I % ((64 / L.w13.lr) * L.w13.ri) == 0 && L.H % ((64 / L.w2.lr) * L.w2.ri) == 0;
   if (!tiled) {

@@ -1,35 +1,45 @@
-// Prefill path (M > 8): route, per-tier align, grouped GEMM over W13 with a fused
-// SwiGLU, grouped GEMM over W2 with the top-k weight applied per slot, and a
-// fixed-order combine of each token's k slot outputs. Both tiers run in the same
-// launches over their concatenated block lists (local-inference-lab/vllm PR #92,
-// "How it works": both tiers share one routing result and one top-k sum).
+// Prefill path (M > 8): route, per-tier align, then grouped GEMMs over each tier's
+// padded expert blocks: W13 with a fused SwiGLU, W2 with the top-k weight applied per
+// slot, and a fixed-order combine of each token's k slot outputs. Both tiers run in
+// the same launches over their concatenated block lists (local-inference-lab/vllm PR
+// #92, "How it works": both tiers share one routing result and one top-k sum).
 //
-// GEMM tile: block_m rows (slots of one expert) x 64 output columns, K in steps of
-// 64 (one NF3 group). The weight tile is decoded once per step into LDS as 16-bit
-// values, the activation tile is gathered into LDS, and each wave runs 16x16x32
-// MFMAs over its 16 output columns.
-//   W13: bf16 MFMA. x is bf16. NVFP4 e2m1 * E4M3 and MXFP4 e2m1 * 2^(b-127) are exact
-//        in bf16; NF3 tiles hold scaled levels (kNF3TableScaleBf16) and each step's
-//        fp32 partial is multiplied by the group scale before accumulation. The
-//        epilogue applies the per-tensor factor, SwiGLU, and stores h as fp16
-//        (saturated at +-65504: 11 significant bits for the W2 input).
-//   W2:  fp16 MFMA. NVFP4 e2m1 * E4M3 is exact in fp16 (2^-10 .. 2688); MXFP4 rows are
-//        stored as e2m1 * 2^(b - bref) with bref the row's largest block exponent, and
-//        2^(bref - 127) returns in the epilogue; NF3 as in W13 with the fp16 table. The
-//        epilogue multiplies by the routing weight and stores fp32 per-slot outputs.
+// GEMM: a block computes BM slots x 128 weight rows (W13: 64 gate rows and the
+// matching 64 up rows; W2: 128 output columns) over K in steps of 64 (one NF3 group),
+// with fp16 16x16x32 MFMAs. Four waves split the tile 2 x 2 (1 x 4 for BM = 16). LDS
+// holds two stages of the activation and the decoded weight tile: while one stage
+// feeds the MFMAs, the next step's raw weights and activations are already in
+// registers and are decoded into the other stage afterwards, one barrier per step.
+//
+// Precision. The MFMAs run on fp16 operands with fp32 accumulation.
+//   x:  bf16 tokens are converted once per token to fp16 times 2^-e, e chosen so the
+//       token's largest |x| lands in [2^14, 2^15) (exact for every element within 2^29
+//       of it); 2^e returns in the W13 epilogue.
+//   h:  W13's SwiGLU output is stored as fp16, saturated at +-65504.
+//   NVFP4: e2m1 * E4M3 has at most 6 significant bits and lies in [2^-10, 2688]: the
+//       conversion applies the scale's power of two, a packed fp16 multiply its 1.m
+//       factor, both exact. The per-tensor fp32 scale returns in the epilogue.
+//   MXFP4: e2m1 * 2^(b - bref) with bref the row's largest E8M0 byte (exact unless a
+//       block is 2^24 below the row's largest); 2^(bref - 127) returns in the epilogue.
+//   NF3: the 64-entry table holds scaled level pairs (kNF3TableScaleF16); each K step
+//       is one group, so its two MFMAs accumulate into a fresh fp32 partial that is
+//       multiplied by the group's fp16 scale before it joins the accumulator.
 #include "device_common.h"
 #include "hmoe_internal.h"
 
 namespace hmoe {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kPfThreads = 256;
-constexpr int kBK = 64;
-constexpr int kLds = kBK + 8;  // 16-bit elements per LDS row (16-byte pad)
-constexpr int kBN = 64;        // output columns per block
+constexpr int kBK = 64;         // K per step (one NF3 group)
+constexpr int kBN = 128;        // weight rows per tile
+
+// LDS tiles hold rows of 64 16-bit values (eight 16-byte chunks) with chunk c of row
+// r stored at chunk c ^ (r & 7): the 16-byte MFMA operand reads of 16 consecutive
+// rows then spread over all banks.
+__device__ __forceinline__ int swz(int r, int c) { return 8 * (c ^ (r & 7)); }
 
 struct PrefillArgs {
   const uint8_t* kq;
@@ -40,7 +50,8 @@ struct PrefillArgs {
   int kept_fmt;
   int rows_w;  // rows of the weight tensor per expert
   int K;
-  const uint16_t* act;   // W13: x bf16 [M, H]; W2: h fp16 [cap0 + cap1, I]
+  const uint16_t* act;   // W13: x fp16 [M, H] (scaled per token); W2: h fp16 [cap0 + cap1, I]
+  const int32_t* xe;     // W13: per-token exponent of the x scaling
   int k, nslot;
   const int32_t* slots[2];
   const int32_t* bexp[2];
@@ -55,56 +66,218 @@ struct PrefillArgs {
   const float* topk_w;
 };
 
-template <bool F16>
-__device__ __forceinline__ uint32_t pack16(float a, float b) {
-  if constexpr (F16) return pack_f16(a, b);
-  else return pack_bf16(a, b);
+enum : int { kPfNvfp4 = 0, kPfMxfp4 = 1, kPfNf3 = 2 };
+
+// Raw weights of one 32-element unit: codes and the scale word(s) it needs.
+struct RawUnit {
+  uint4 q;
+  uint32_t s;
+};
+
+template <int FMT>
+__device__ __forceinline__ RawUnit load_unit(const PrefillArgs& a, size_t grow, int ku) {
+  RawUnit u;
+  if constexpr (FMT == kPfNf3) {
+    const uint3 v = *reinterpret_cast<const uint3*>(a.nq + grow * (3 * a.K / 8) + 12 * ku);
+    u.q = make_uint4(v.x, v.y, v.z, 0u);
+    u.s = a.ns[grow * (a.K / 64) + (ku >> 1)];
+  } else if constexpr (FMT == kPfNvfp4) {
+    u.q = *reinterpret_cast<const uint4*>(a.kq + grow * (a.K / 2) + 16 * ku);
+    u.s = *reinterpret_cast<const uint16_t*>(a.ks + grow * (a.K / 16) + 2 * ku);
+  } else {
+    u.q = *reinterpret_cast<const uint4*>(a.kq + grow * (a.K / 2) + 16 * ku);
+    u.s = a.ks[grow * (a.K / 32) + ku];
+  }
+  return u;
+}
+
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t v, f16x2 m) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) * m);
+}
+
+// NVFP4 16-element block (two code words) -> 8 fp16 pairs, exact (see the header).
+__device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32_t sbyte,
+                                                uint32_t* w) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8(sbyte, 0);
+  const float mu32 = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  const _Float16 mu = (s == 0.0f) ? (_Float16)0.0f : (s != s ? (_Float16)s : (_Float16)mu32);
+  const f16x2 m = {mu, mu};
+  w[0] = mul_f16x2(e2m1x2_f16<0>(q0, s), m);
+  w[1] = mul_f16x2(e2m1x2_f16<1>(q0, s), m);
+  w[2] = mul_f16x2(e2m1x2_f16<2>(q0, s), m);
+  w[3] = mul_f16x2(e2m1x2_f16<3>(q0, s), m);
+  w[4] = mul_f16x2(e2m1x2_f16<0>(q1, s), m);
+  w[5] = mul_f16x2(e2m1x2_f16<1>(q1, s), m);
+  w[6] = mul_f16x2(e2m1x2_f16<2>(q1, s), m);
+  w[7] = mul_f16x2(e2m1x2_f16<3>(q1, s), m);
+}
+
+// One unit -> 16 fp16 pairs. ref: the row's MXFP4 reference byte; lut: NF3 pair table.
+template <int FMT>
+__device__ __forceinline__ void decode_unit(const RawUnit& u, int ref, const uint32_t* lut,
+                                            uint32_t (&w)[16]) {
+  if constexpr (FMT == kPfNvfp4) {
+    nvfp4_block_f16(u.q.x, u.q.y, u.s & 0xFFu, w);
+    nvfp4_block_f16(u.q.z, u.q.w, (u.s >> 8) & 0xFFu, w + 8);
+  } else if constexpr (FMT == kPfMxfp4) {
+    const int b = max((int)u.s - ref + 127, 0);
+    const float so = e8m0_scale_operand((uint32_t)b);
+    const uint32_t qq[4] = {u.q.x, u.q.y, u.q.z, u.q.w};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      w[4 * v + 0] = e2m1x2_f16<0>(qq[v], so);
+      w[4 * v + 1] = e2m1x2_f16<1>(qq[v], so);
+      w[4 * v + 2] = e2m1x2_f16<2>(qq[v], so);
+      w[4 * v + 3] = e2m1x2_f16<3>(qq[v], so);
+    }
+  } else {
+    // lut points at this lane's column of the [field][32] table
+    const uint32_t d0 = u.q.x, d1 = u.q.y, d2 = u.q.z;
+    w[0] = lut[nf3_pair_field<0>(d0, d1, d2) << 5];   w[1] = lut[nf3_pair_field<1>(d0, d1, d2) << 5];
+    w[2] = lut[nf3_pair_field<2>(d0, d1, d2) << 5];   w[3] = lut[nf3_pair_field<3>(d0, d1, d2) << 5];
+    w[4] = lut[nf3_pair_field<4>(d0, d1, d2) << 5];   w[5] = lut[nf3_pair_field<5>(d0, d1, d2) << 5];
+    w[6] = lut[nf3_pair_field<6>(d0, d1, d2) << 5];   w[7] = lut[nf3_pair_field<7>(d0, d1, d2) << 5];
+    w[8] = lut[nf3_pair_field<8>(d0, d1, d2) << 5];   w[9] = lut[nf3_pair_field<9>(d0, d1, d2) << 5];
+    w[10] = lut[nf3_pair_field<10>(d0, d1, d2) << 5]; w[11] = lut[nf3_pair_field<11>(d0, d1, d2) << 5];
+    w[12] = lut[nf3_pair_field<12>(d0, d1, d2) << 5]; w[13] = lut[nf3_pair_field<13>(d0, d1, d2) << 5];
+    w[14] = lut[nf3_pair_field<14>(d0, d1, d2) << 5]; w[15] = lut[nf3_pair_field<15>(d0, d1, d2) << 5];
+  }
 }
 
 template <int BM, bool W13>
-__global__ __launch_bounds__(kPfThreads) void grouped_gemm_kernel(PrefillArgs a) {
-  constexpr bool F16 = !W13;                   // W2 runs on fp16
-  constexpr int BROWS = W13 ? 2 * kBN : kBN;   // weight rows per tile
-  constexpr int NT = W13 ? 2 : 1;              // MFMA column tiles per wave
-  constexpr int MT = BM / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM][kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BROWS][kLds];
-  __shared__ uint32_t lutp[64];     // scaled NF3 level pairs (16-bit each)
-  __shared__ float sS[BROWS];       // NF3 group scale of each tile row, this step
-  __shared__ int sRef[BROWS];       // MXFP4 (W2): row reference exponent
+struct GemmShape {
+  static constexpr int WAVES_M = BM >= 32 ? 2 : 1;
+  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int MT = BM / WAVES_M / 16;     // 16-row MFMA tiles per wave
+  static constexpr int NT = kBN / WAVES_N / 16;    // 16-column MFMA tiles per wave
+  static constexpr int A_CHUNKS = BM * (kBK / 8);  // 16-byte pieces of an activation tile
+  static constexpr int A_PER = (A_CHUNKS + kPfThreads - 1) / kPfThreads;
+};
+
+// Weight row (within the 128-row tile) of MFMA column tile nt of wave wn. W13 pairs
+// gate tile nt with up tile nt + NT/2 (same h columns, same lane).
+template <int BM, bool W13>
+__device__ __forceinline__ int tile_row(int wn, int nt) {
+  using S = GemmShape<BM, W13>;
+  if constexpr (W13) {
+    constexpr int HALF = S::NT / 2;
+    const int base = wn * (kBN / 2 / S::WAVES_N);
+    return nt < HALF ? base + 16 * nt : kBN / 2 + base + 16 * (nt - HALF);
+  } else {
+    return wn * (kBN / S::WAVES_N) + 16 * nt;
+  }
+}
+
+// LDS of one GEMM block
+template <int BM>
+struct GemmSmem {
+  __attribute__((aligned(16))) uint16_t As[2][BM][kBK];   // activation tile, two stages
+  __attribute__((aligned(16))) uint16_t Bs[2][kBN][kBK];  // decoded weight tile, two stages
+  uint32_t lut[64 * 32];  // NF3: fp16 pairs of scaled levels, [pair field][lane % 32]
+  float sS[2][kBN];       // NF3: group scale of each tile row, per stage
+  int sRef[kBN];          // MXFP4: row reference byte
+};
+
+template <int BM, bool W13, int FMT>
+__device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b, int loc,
+                                          GemmSmem<BM>& sm) {
+  using S = GemmShape<BM, W13>;
+  constexpr int MT = S::MT, NT = S::NT;
+  auto& As = sm.As;
+  auto& Bs = sm.Bs;
+  auto& lut = sm.lut;
+  auto& sS = sm.sS;
+  auto& sRef = sm.sRef;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
-
-  const int by = blockIdx.x;
-  const int tier = by < a.nblk0 ? 0 : 1;
-  const int b = tier ? by - a.nblk0 : by;
-  // npad and the block table come from the align stage; clamp to this launch's grid
-  // and the tier's expert count so stale scratch cannot index out of range
-  if (b * BM >= a.npad[tier][0] || b >= (tier ? a.nblk1 : a.nblk0)) return;
-  const int loc = a.bexp[tier][b];
-  if ((unsigned)loc >= (unsigned)(tier ? a.E3 : a.E4)) return;
-  const bool nf3 = tier == HMOE_TIER_NF3;
-  const bool mx = !nf3 && a.kept_fmt == HMOE_KEPT_MXFP4;
-  const int n0 = blockIdx.y * kBN;
+  const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
+  const int n0 = blockIdx.x * (W13 ? kBN / 2 : kBN);
   const int32_t* bslots = a.slots[tier] + (size_t)b * BM;
   const size_t hbase = (size_t)(tier ? a.hrow1 : 0) + (size_t)b * BM;
+  const int steps = a.K / kBK;
 
-  if (tid < 64) {
-    const float c = F16 ? kNF3TableScaleF16 : kNF3TableScaleBf16;
-    lutp[tid] = pack16<F16>(nf3_level(tid & 7) * c, nf3_level(tid >> 3) * c);
-  }
-  if (F16 && mx) {
-    // largest E8M0 byte of each of the tile's rows (over the whole K)
-    for (int r = wave; r < BROWS; r += kPfThreads / kWave) {
-      const uint8_t* srow = a.ks + ((size_t)loc * a.rows_w + n0 + r) * (a.K / 32);
-      int m = 0;
-      for (int i = lane; i < a.K / 32; i += kWave) m = max(m, (int)srow[i]);
+  // this thread's weight unit of every step: tile row r, half uu
+  const int r = tid >> 1, uu = tid & 1;
+  int wrow;
+  if (W13) wrow = r < kBN / 2 ? n0 + r : a.I + n0 + (r - kBN / 2);
+  else wrow = n0 + r;
+  const size_t grow = (size_t)loc * a.rows_w + wrow;
+
+  // activation rows of this thread (16-byte piece c of row m), fixed over K
+  const uint16_t* arow[S::A_PER];
+  int apiece[S::A_PER];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
-      if (lane == 0) sRef[r] = m;
+  for (int i = 0; i < S::A_PER; ++i) {
+    const int c = tid + kPfThreads * i;
+    const int m = c / (kBK / 8);
+    apiece[i] = c - m * (kBK / 8);
+    arow[i] = nullptr;
+    if (c < S::A_CHUNKS) {
+      if (W13) {
+        const int slot = bslots[m];
+        if ((unsigned)slot < (unsigned)a.nslot) arow[i] = a.act + (size_t)(slot / a.k) * a.K;
+      } else {
+        arow[i] = a.act + (hbase + m) * a.K;
+      }
     }
   }
+
+  if (FMT == kPfNf3) {
+    // thread t writes fields (t >> 5) + 8j of column t & 31: low code t >> 5, high j
+    const float lo = nf3_level(tid >> 5) * kNF3TableScaleF16;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      lut[((tid >> 5) + 8 * j) * 32 + (tid & 31)] =
+          pack_f16(lo, __uint_as_float(kNF3Bits[j]) * kNF3TableScaleF16);
+  }
+  if (FMT == kPfMxfp4) {
+    // largest E8M0 byte of each tile row over the whole K
+    for (int rr = wave; rr < kBN; rr += kPfThreads / kWave) {
+      int row;
+      if (W13) row = rr < kBN / 2 ? n0 + rr : a.I + n0 + (rr - kBN / 2);
+      else row = n0 + rr;
+      const uint8_t* srow = a.ks + ((size_t)loc * a.rows_w + row) * (a.K / 32);
+      int m = 0;
+      for (int i = lane; i < a.K / 32; i += kWave) m = max(m, (int)srow[i]);
+      m = max(m, __shfl_xor(m, 32));
+      m = max(m, __shfl_xor(m, 16));
+      m = max(m, __shfl_xor(m, 8));
+      m = max(m, __shfl_xor(m, 4));
+      m = max(m, __shfl_xor(m, 2));
+      m = max(m, __shfl_xor(m, 1));
+      if (lane == 0) sRef[rr] = m;
+    }
+  }
+
+  // registers of the step in flight
+  uint4 av[S::A_PER];
+  RawUnit wu;
+  auto load_step = [&](int st) {
+    const int k0 = st * kBK;
+#pragma unroll
+    for (int i = 0; i < S::A_PER; ++i)
+      av[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + 8 * apiece[i])
+                      : make_uint4(0u, 0u, 0u, 0u);
+    wu = load_unit<FMT>(a, grow, 2 * st + uu);
+  };
+  auto store_step = [&](int buf, int ref) {
+#pragma unroll
+    for (int i = 0; i < S::A_PER; ++i) {
+      const int c = tid + kPfThreads * i;
+      if (c < S::A_CHUNKS) {
+        const int m = c / (kBK / 8);
+        *reinterpret_cast<uint4*>(&As[buf][m][swz(m, apiece[i])]) = av[i];
+      }
+    }
+    uint32_t w[16];
+    decode_unit<FMT>(wu, ref, lut + (lane & 31), w);
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 0)]) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 1)]) = make_uint4(w[4], w[5], w[6], w[7]);
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 2)]) = make_uint4(w[8], w[9], w[10], w[11]);
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 3)]) = make_uint4(w[12], w[13], w[14], w[15]);
+    if (FMT == kPfNf3 && uu == 0) sS[buf][r] = fp16_to_f32(wu.s);
+  };
 
   f32x4 acc[MT][NT];
 #pragma unroll
@@ -112,128 +285,46 @@ __global__ __launch_bounds__(kPfThreads) void grouped_gemm_kernel(PrefillArgs a)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < a.K; k0 += kBK) {
-    __syncthreads();
-    // activation tile: BM rows x 64 16-bit values, 16-byte chunks
-    for (int c = tid; c < BM * (kBK / 8); c += kPfThreads) {
-      const int m = c / (kBK / 8);
-      const int ch = c - m * (kBK / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (W13) {
-        const int slot = bslots[m];
-        if ((unsigned)slot < (unsigned)a.nslot)
-          v = *reinterpret_cast<const uint4*>(a.act + (size_t)(slot / a.k) * a.K + k0 + 8 * ch);
-      } else {
-        v = *reinterpret_cast<const uint4*>(a.act + (hbase + m) * a.K + k0 + 8 * ch);
-      }
-      *reinterpret_cast<uint4*>(&As[m][8 * ch]) = v;
-    }
-    // weight tile: BROWS rows x 2 units of 32
-    for (int u = tid; u < BROWS * 2; u += kPfThreads) {
-      const int r = u >> 1;
-      const int uu = u & 1;
-      int row;
-      if (W13) row = r < kBN ? n0 + r : a.I + n0 + (r - kBN);
-      else row = n0 + r;
-      const size_t grow = (size_t)loc * a.rows_w + row;
-      const int ku = k0 / 32 + uu;
-      uint32_t w[16];
-      if (nf3) {
-        const uint32_t* p = reinterpret_cast<const uint32_t*>(a.nq + grow * (3 * a.K / 8) + 12 * ku);
-        const uint32_t d0 = p[0], d1 = p[1], d2 = p[2];
-        w[0] = lutp[nf3_pair_field<0>(d0, d1, d2)]; w[1] = lutp[nf3_pair_field<1>(d0, d1, d2)];
-        w[2] = lutp[nf3_pair_field<2>(d0, d1, d2)]; w[3] = lutp[nf3_pair_field<3>(d0, d1, d2)];
-        w[4] = lutp[nf3_pair_field<4>(d0, d1, d2)]; w[5] = lutp[nf3_pair_field<5>(d0, d1, d2)];
-        w[6] = lutp[nf3_pair_field<6>(d0, d1, d2)]; w[7] = lutp[nf3_pair_field<7>(d0, d1, d2)];
-        w[8] = lutp[nf3_pair_field<8>(d0, d1, d2)]; w[9] = lutp[nf3_pair_field<9>(d0, d1, d2)];
-        w[10] = lutp[nf3_pair_field<10>(d0, d1, d2)]; w[11] = lutp[nf3_pair_field<11>(d0, d1, d2)];
-        w[12] = lutp[nf3_pair_field<12>(d0, d1, d2)]; w[13] = lutp[nf3_pair_field<13>(d0, d1, d2)];
-        w[14] = lutp[nf3_pair_field<14>(d0, d1, d2)]; w[15] = lutp[nf3_pair_field<15>(d0, d1, d2)];
-        if (uu == 0) sS[r] = fp16_to_f32(a.ns[grow * (a.K / 64) + k0 / 64]);
-      } else {
-        const uint4 q = *reinterpret_cast<const uint4*>(a.kq + grow * (a.K / 2) + 16 * ku);
-        const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
-        if (!mx) {
-          const uint32_t sc = *reinterpret_cast<const uint16_t*>(a.ks + grow * (a.K / 16) + 2 * ku);
-          const float s0 = e4m3_to_f32<0>(sc);
-          const float s1 = e4m3_to_f32<1>(sc);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float s = v < 2 ? s0 : s1;
-            const f32x2 p0 = e2m1x2_f32<0>(qq[v], 1.0f);
-            const f32x2 p1 = e2m1x2_f32<1>(qq[v], 1.0f);
-            const f32x2 p2 = e2m1x2_f32<2>(qq[v], 1.0f);
-            const f32x2 p3 = e2m1x2_f32<3>(qq[v], 1.0f);
-            w[4 * v + 0] = pack16<F16>(p0[0] * s, p0[1] * s);
-            w[4 * v + 1] = pack16<F16>(p1[0] * s, p1[1] * s);
-            w[4 * v + 2] = pack16<F16>(p2[0] * s, p2[1] * s);
-            w[4 * v + 3] = pack16<F16>(p3[0] * s, p3[1] * s);
-          }
-        } else if (!F16) {
-          const float so = e8m0_scale_operand(a.ks[grow * (a.K / 32) + ku]);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            w[4 * v + 0] = e2m1x2_bf16<0>(qq[v], so);
-            w[4 * v + 1] = e2m1x2_bf16<1>(qq[v], so);
-            w[4 * v + 2] = e2m1x2_bf16<2>(qq[v], so);
-            w[4 * v + 3] = e2m1x2_bf16<3>(qq[v], so);
-          }
-        } else {
-          const int be = (int)a.ks[grow * (a.K / 32) + ku] - sRef[r];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const f32x2 p0 = e2m1x2_f32<0>(qq[v], 1.0f);
-            const f32x2 p1 = e2m1x2_f32<1>(qq[v], 1.0f);
-            const f32x2 p2 = e2m1x2_f32<2>(qq[v], 1.0f);
-            const f32x2 p3 = e2m1x2_f32<3>(qq[v], 1.0f);
-            w[4 * v + 0] = pack_f16(__builtin_ldexpf(p0[0], be), __builtin_ldexpf(p0[1], be));
-            w[4 * v + 1] = pack_f16(__builtin_ldexpf(p1[0], be), __builtin_ldexpf(p1[1], be));
-            w[4 * v + 2] = pack_f16(__builtin_ldexpf(p2[0], be), __builtin_ldexpf(p2[1], be));
-            w[4 * v + 3] = pack_f16(__builtin_ldexpf(p3[0], be), __builtin_ldexpf(p3[1], be));
-          }
-        }
-      }
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[r][32 * uu]);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      dst[2] = make_uint4(w[8], w[9], w[10], w[11]);
-      dst[3] = make_uint4(w[12], w[13], w[14], w[15]);
-    }
-    __syncthreads();
+  load_step(0);
+  __syncthreads();  // table and reference bytes
+  const int ref = FMT == kPfMxfp4 ? sRef[r] : 0;
+  store_step(0, ref);
+  __syncthreads();
+
+  for (int st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < steps) load_step(st + 1);
     f32x4 part[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) part[mt][nt] = nf3 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][nt];
+      for (int nt = 0; nt < NT; ++nt)
+        part[mt][nt] = FMT == kPfNf3 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][nt];
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
-      const int kk = ks * 32 + 8 * (lane >> 4);
+      // chunk 4 ks + lane / 16 of rows lane % 16 (row bases are multiples of 16)
+      const int kk = swz(lane, 4 * ks + (lane >> 4));
       uint4 bq[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        bq[nt] = *reinterpret_cast<const uint4*>(&Bs[nt * kBN + 16 * wave + (lane & 15)][kk]);
+        bq[nt] = *reinterpret_cast<const uint4*>(&Bs[buf][tile_row<BM, W13>(wn, nt) + (lane & 15)][kk]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 aq = *reinterpret_cast<const uint4*>(&As[mt * 16 + (lane & 15)][kk]);
+        const uint4 aq = *reinterpret_cast<const uint4*>(&As[buf][(wm * MT + mt) * 16 + (lane & 15)][kk]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if constexpr (F16)
-            part[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(f16x8, aq), __builtin_bit_cast(f16x8, bq[nt]), part[mt][nt], 0, 0, 0);
-          else
-            part[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, aq), __builtin_bit_cast(bf16x8, bq[nt]), part[mt][nt], 0, 0, 0);
-        }
+        for (int nt = 0; nt < NT; ++nt)
+          part[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8, aq), __builtin_bit_cast(f16x8, bq[nt]), part[mt][nt], 0, 0, 0);
       }
     }
-    if (nf3) {
+    if constexpr (FMT == kPfNf3) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float s = sS[nt * kBN + 16 * wave + (lane & 15)];
+        const float s = sS[buf][tile_row<BM, W13>(wn, nt) + (lane & 15)];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf(s, part[mt][nt][r], acc[mt][nt][r]);
+          for (int q = 0; q < 4; ++q) acc[mt][nt][q] = __builtin_fmaf(s, part[mt][nt][q], acc[mt][nt][q]);
       }
     } else {
 #pragma unroll
@@ -241,30 +332,80 @@ __global__ __launch_bounds__(kPfThreads) void grouped_gemm_kernel(PrefillArgs a)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = part[mt][nt];
     }
+    if (st + 1 < steps) store_step(buf ^ 1, ref);
+    __syncthreads();
   }
-  // epilogue: lane holds rows 4*(lane/16)+r of each 16-row tile, column lane%16
-  const int col = 16 * wave + (lane & 15);
-  const int n = n0 + col;
-  float g;
-  if (nf3) g = 1.0f / (F16 ? kNF3TableScaleF16 : kNF3TableScaleBf16);
-  else if (!mx) g = a.kg[loc];
-  else g = F16 ? e8m0_to_f32((uint32_t)sRef[col]) : 1.0f;
+
+  // epilogue: lane holds rows 4 * (lane / 16) + q of each 16-row tile, column lane % 16
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int nt = 0; nt < (W13 ? NT / 2 : NT); ++nt) {
+    const int tr = tile_row<BM, W13>(wn, nt) + (lane & 15);   // gate / W2 tile row
+    auto col_factor = [&](int trow) {
+      if (FMT == kPfNf3) return 1.0f / kNF3TableScaleF16;
+      if (FMT == kPfNvfp4) return a.kg[loc];
+      return e8m0_to_f32((uint32_t)sRef[trow]);
+    };
+    const float gf = col_factor(tr);
+    const float uf = W13 ? col_factor(tile_row<BM, W13>(wn, nt + NT / 2) + (lane & 15)) : 0.0f;
+    const int n = n0 + (W13 ? tr : tr);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mt * 16 + 4 * (lane >> 4) + r;
-      if (W13) {
-        const float gate = acc[mt][0][r] * g;
-        const float up = acc[mt][NT - 1][r] * g;
-        const float h = fminf(fmaxf(silu(gate) * up, -65504.0f), 65504.0f);
-        a.h_out[(hbase + m) * a.I + n] = (uint16_t)(pack_f16(h, 0.0f) & 0xFFFFu);
-      } else {
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = (wm * MT + mt) * 16 + 4 * (lane >> 4) + q;
         const int slot = bslots[m];
-        if ((unsigned)slot < (unsigned)a.nslot) a.o_out[(size_t)slot * a.H + n] = acc[mt][0][r] * g * a.topk_w[slot];
+        if (W13) {
+          // x was scaled by 2^-xe[token]
+          const float xs = (unsigned)slot < (unsigned)a.nslot ? __builtin_ldexpf(1.0f, a.xe[slot / a.k]) : 0.0f;
+          const float gate = acc[mt][nt][q] * gf * xs;
+          const float up = acc[mt][nt + NT / 2][q] * uf * xs;
+          const float h = fminf(fmaxf(silu(gate) * up, -65504.0f), 65504.0f);
+          a.h_out[(hbase + m) * a.I + n] = (uint16_t)(pack_f16(h, 0.0f) & 0xFFFFu);
+        } else {
+          if ((unsigned)slot < (unsigned)a.nslot)
+            a.o_out[(size_t)slot * a.H + n] = acc[mt][nt][q] * gf * a.topk_w[slot];
+        }
       }
     }
   }
+}
+
+template <int BM, bool W13>
+__global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs a) {
+  // blockIdx.x walks the output columns of one expert block, so the blocks that run
+  // together share its activation rows in cache and stream adjacent weight rows
+  const int by = blockIdx.y;
+  const int tier = by < a.nblk0 ? 0 : 1;
+  const int b = tier ? by - a.nblk0 : by;
+  // npad and the block table come from the align stage; clamp to this launch's grid
+  // and the tier's expert count so stale scratch cannot index out of range
+  if (b * BM >= a.npad[tier][0] || b >= (tier ? a.nblk1 : a.nblk0)) return;
+  const int loc = a.bexp[tier][b];
+  if ((unsigned)loc >= (unsigned)(tier ? a.E3 : a.E4)) return;
+  __shared__ GemmSmem<BM> sm;
+  if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3>(a, tier, b, loc, sm);
+  else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4>(a, tier, b, loc, sm);
+  else gemm_tile<BM, W13, kPfMxfp4>(a, tier, b, loc, sm);
+}
+
+// x16[t] = fp16(x[t] * 2^-e[t]), e[t] putting the token's largest |x| in [2^14, 2^15)
+__global__ __launch_bounds__(256) void prefill_x16_kernel(const uint16_t* __restrict__ x, int H,
+                                                          uint16_t* __restrict__ x16,
+                                                          int32_t* __restrict__ xe) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const uint16_t* row = x + (size_t)t * H;
+  float mx = 0.0f;
+  for (int i = threadIdx.x; i < H; i += 256) mx = fmaxf(mx, fabsf(__uint_as_float((uint32_t)row[i] << 16)));
+  mx = group_max<kWave>(mx);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int ef = (int)((__float_as_uint(mx) >> 23) & 0xFF);
+  const int e = mx > 0.0f ? (ef == 0 ? -126 : ef - 127) - 14 : 0;
+  for (int i = threadIdx.x; i < H; i += 256)
+    x16[(size_t)t * H + i] = (uint16_t)(pack_f16(__builtin_ldexpf(__uint_as_float((uint32_t)row[i] << 16), -e), 0.0f) & 0xFFFFu);
+  if (threadIdx.x == 0) xe[t] = e;
 }
 
 // y[t, n] = sum_j o[t*k + j, n] in fixed j order (the routing weight is already in o)
@@ -321,18 +462,22 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
   a.H = L.H;
   uint16_t* h = reinterpret_cast<uint16_t*>(base + P.h_pre);
   float* o = reinterpret_cast<float*>(base + P.o_pre);
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base + P.x16_pre);
+  int32_t* xe = reinterpret_cast<int32_t*>(base + P.xe_pre);
   const int nblk = a.nblk0 + a.nblk1;
   if (stage == HMOE_STAGE_W13) {
+    hipLaunchKernelGGL(prefill_x16_kernel, dim3(M), dim3(256), 0, s, x, L.H, x16, xe);
     PrefillArgs b = a;
     b.kq = W.kept_w13_q; b.ks = W.kept_w13_s; b.kg = W.kept_w13_g;
     b.nq = W.nf3_w13_q; b.ns = W.nf3_w13_s;
     b.rows_w = 2 * L.I;
     b.K = L.H;
-    b.act = x;
+    b.act = x16;
+    b.xe = xe;
     b.h_out = h;
     GemmFn fn = pick_gemm<true>(bm);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(nblk, L.I / kBN), dim3(kPfThreads), 0, s, b);
+    hipLaunchKernelGGL(fn, dim3(L.I / (kBN / 2), nblk), dim3(kPfThreads), 0, s, b);
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_W2) {
@@ -346,7 +491,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     c.topk_w = w;
     GemmFn fn = pick_gemm<false>(bm);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(nblk, L.H / kBN), dim3(kPfThreads), 0, s, c);
+    hipLaunchKernelGGL(fn, dim3(L.H / kBN, nblk), dim3(kPfThreads), 0, s, c);
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_COMBINE) {
