@@ -171,6 +171,11 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
   L.max_distinct = std::min(hmoe::kDecodeMaxM * L.k, L.E);
   L.cap[0] = tier_capacity(L.max_tokens, L.k, L.E4, L.block_m);
   L.cap[1] = tier_capacity(L.max_tokens, L.k, L.E3, L.block_m);
+  // the prefill GEMMs address activation rows with 32-bit element offsets
+  if ((long)L.max_tokens * L.H >= (1L << 31) || (long)(L.cap[0] + L.cap[1]) * L.I >= (1L << 31)) {
+    delete h;
+    return fail(HMOE_ERR_UNSUPPORTED, "max_tokens too large for this layer's prefill buffers");
+  }
   // the prefill GEMMs put the expert blocks of both tiers on the grid's y axis
   if ((long)(L.cap[0] + L.cap[1]) / L.block_m > 65535) {
     delete h;

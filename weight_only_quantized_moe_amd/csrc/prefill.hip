@@ -68,80 +68,8 @@ struct PrefillArgs {
 
 enum : int { kPfNvfp4 = 0, kPfMxfp4 = 1, kPfNf3 = 2 };
 
-// Raw weights of one 32-element unit: codes and the scale word(s) it needs.
-struct RawUnit {
-  uint4 q;
-  uint32_t s;
-};
-
-template <int FMT>
-__device__ __forceinline__ RawUnit load_unit(const PrefillArgs& a, size_t grow, int ku) {
-  RawUnit u;
-  if constexpr (FMT == kPfNf3) {
-    const uint3 v = *reinterpret_cast<const uint3*>(a.nq + grow * (3 * a.K / 8) + 12 * ku);
-    u.q = make_uint4(v.x, v.y, v.z, 0u);
-    u.s = a.ns[grow * (a.K / 64) + (ku >> 1)];
-  } else if constexpr (FMT == kPfNvfp4) {
-    u.q = *reinterpret_cast<const uint4*>(a.kq + grow * (a.K / 2) + 16 * ku);
-    u.s = *reinterpret_cast<const uint16_t*>(a.ks + grow * (a.K / 16) + 2 * ku);
-  } else {
-    u.q = *reinterpret_cast<const uint4*>(a.kq + grow * (a.K / 2) + 16 * ku);
-    u.s = a.ks[grow * (a.K / 32) + ku];
-  }
-  return u;
-}
-
 __device__ __forceinline__ uint32_t mul_f16x2(uint32_t v, f16x2 m) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) * m);
-}
-
-// NVFP4 16-element block (two code words) -> 8 fp16 pairs, exact (see the header).
-__device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32_t sbyte,
-                                                uint32_t* w) {
-  const float s = __builtin_amdgcn_cvt_f32_fp8(sbyte, 0);
-  const float mu32 = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
-  const _Float16 mu = (s == 0.0f) ? (_Float16)0.0f : (s != s ? (_Float16)s : (_Float16)mu32);
-  const f16x2 m = {mu, mu};
-  w[0] = mul_f16x2(e2m1x2_f16<0>(q0, s), m);
-  w[1] = mul_f16x2(e2m1x2_f16<1>(q0, s), m);
-  w[2] = mul_f16x2(e2m1x2_f16<2>(q0, s), m);
-  w[3] = mul_f16x2(e2m1x2_f16<3>(q0, s), m);
-  w[4] = mul_f16x2(e2m1x2_f16<0>(q1, s), m);
-  w[5] = mul_f16x2(e2m1x2_f16<1>(q1, s), m);
-  w[6] = mul_f16x2(e2m1x2_f16<2>(q1, s), m);
-  w[7] = mul_f16x2(e2m1x2_f16<3>(q1, s), m);
-}
-
-// One unit -> 16 fp16 pairs. ref: the row's MXFP4 reference byte; lut: NF3 pair table.
-template <int FMT>
-__device__ __forceinline__ void decode_unit(const RawUnit& u, int ref, const uint32_t* lut,
-                                            uint32_t (&w)[16]) {
-  if constexpr (FMT == kPfNvfp4) {
-    nvfp4_block_f16(u.q.x, u.q.y, u.s & 0xFFu, w);
-    nvfp4_block_f16(u.q.z, u.q.w, (u.s >> 8) & 0xFFu, w + 8);
-  } else if constexpr (FMT == kPfMxfp4) {
-    const int b = max((int)u.s - ref + 127, 0);
-    const float so = e8m0_scale_operand((uint32_t)b);
-    const uint32_t qq[4] = {u.q.x, u.q.y, u.q.z, u.q.w};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      w[4 * v + 0] = e2m1x2_f16<0>(qq[v], so);
-      w[4 * v + 1] = e2m1x2_f16<1>(qq[v], so);
-      w[4 * v + 2] = e2m1x2_f16<2>(qq[v], so);
-      w[4 * v + 3] = e2m1x2_f16<3>(qq[v], so);
-    }
-  } else {
-    // lut points at this lane's column of the [field][32] table
-    const uint32_t d0 = u.q.x, d1 = u.q.y, d2 = u.q.z;
-    w[0] = lut[nf3_pair_field<0>(d0, d1, d2) << 5];   w[1] = lut[nf3_pair_field<1>(d0, d1, d2) << 5];
-    w[2] = lut[nf3_pair_field<2>(d0, d1, d2) << 5];   w[3] = lut[nf3_pair_field<3>(d0, d1, d2) << 5];
-    w[4] = lut[nf3_pair_field<4>(d0, d1, d2) << 5];   w[5] = lut[nf3_pair_field<5>(d0, d1, d2) << 5];
-    w[6] = lut[nf3_pair_field<6>(d0, d1, d2) << 5];   w[7] = lut[nf3_pair_field<7>(d0, d1, d2) << 5];
-    w[8] = lut[nf3_pair_field<8>(d0, d1, d2) << 5];   w[9] = lut[nf3_pair_field<9>(d0, d1, d2) << 5];
-    w[10] = lut[nf3_pair_field<10>(d0, d1, d2) << 5]; w[11] = lut[nf3_pair_field<11>(d0, d1, d2) << 5];
-    w[12] = lut[nf3_pair_field<12>(d0, d1, d2) << 5]; w[13] = lut[nf3_pair_field<13>(d0, d1, d2) << 5];
-    w[14] = lut[nf3_pair_field<14>(d0, d1, d2) << 5]; w[15] = lut[nf3_pair_field<15>(d0, d1, d2) << 5];
-  }
 }
 
 template <int BM, bool W13>
@@ -168,15 +96,38 @@ __device__ __forceinline__ int tile_row(int wn, int nt) {
   }
 }
 
-// LDS of one GEMM block
+// LDS of one GEMM block: two stages of the activation and the decoded weight tile,
+// the NF3 pair table and the per-row reference exponents.
 template <int BM>
 struct GemmSmem {
-  __attribute__((aligned(16))) uint16_t As[2][BM][kBK];   // activation tile, two stages
-  __attribute__((aligned(16))) uint16_t Bs[2][kBN][kBK];  // decoded weight tile, two stages
+  __attribute__((aligned(16))) uint16_t As[2][BM][kBK];
+  __attribute__((aligned(16))) uint16_t Bs[2][kBN][kBK];
   uint32_t lut[64 * 32];  // NF3: fp16 pairs of scaled levels, [pair field][lane % 32]
-  float sS[2][kBN];       // NF3: group scale of each tile row, per stage
-  int sRef[kBN];          // MXFP4: row reference byte
+  int sRef[kBN];          // MXFP4: largest E8M0 byte; NF3: largest fp16 scale exponent
 };
+
+// One K step of one thread's weight unit (32 elements of one tile row), raw.
+struct WRaw {
+  uint4 q;     // FP4: 16 code bytes; NF3: 12 code bytes in x, y, z
+  uint32_t s;  // NVFP4: two E4M3 bytes; MXFP4: one E8M0 byte; NF3: fp16 group scale
+};
+
+// NVFP4 16-element block (two code words) -> 8 fp16 pairs, exact (see the header).
+__device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32_t sbyte,
+                                                uint32_t* w) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8(sbyte, 0);
+  const float mu32 = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  const _Float16 mu = (s == 0.0f) ? (_Float16)0.0f : (s != s ? (_Float16)s : (_Float16)mu32);
+  const f16x2 m = {mu, mu};
+  w[0] = mul_f16x2(e2m1x2_f16<0>(q0, s), m);
+  w[1] = mul_f16x2(e2m1x2_f16<1>(q0, s), m);
+  w[2] = mul_f16x2(e2m1x2_f16<2>(q0, s), m);
+  w[3] = mul_f16x2(e2m1x2_f16<3>(q0, s), m);
+  w[4] = mul_f16x2(e2m1x2_f16<0>(q1, s), m);
+  w[5] = mul_f16x2(e2m1x2_f16<1>(q1, s), m);
+  w[6] = mul_f16x2(e2m1x2_f16<2>(q1, s), m);
+  w[7] = mul_f16x2(e2m1x2_f16<3>(q1, s), m);
+}
 
 template <int BM, bool W13, int FMT>
 __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b, int loc,
@@ -185,98 +136,143 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   constexpr int MT = S::MT, NT = S::NT;
   auto& As = sm.As;
   auto& Bs = sm.Bs;
-  auto& lut = sm.lut;
-  auto& sS = sm.sS;
-  auto& sRef = sm.sRef;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
   const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
+  const int j = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * (W13 ? kBN / 2 : kBN);
   const int32_t* bslots = a.slots[tier] + (size_t)b * BM;
   const size_t hbase = (size_t)(tier ? a.hrow1 : 0) + (size_t)b * BM;
   const int steps = a.K / kBK;
 
-  // this thread's weight unit of every step: tile row r, half uu
+  // ---- this thread's weight unit of every step: tile row r, half uu (32 elements)
   const int r = tid >> 1, uu = tid & 1;
-  int wrow;
-  if (W13) wrow = r < kBN / 2 ? n0 + r : a.I + n0 + (r - kBN / 2);
-  else wrow = n0 + r;
-  const size_t grow = (size_t)loc * a.rows_w + wrow;
+  const int wrow = W13 ? (r < kBN / 2 ? n0 + r : a.I + n0 + (r - kBN / 2)) : n0 + r;
+  const int RB = FMT == kPfNf3 ? 3 * a.K / 8 : a.K / 2;  // code bytes per row
+  const int CB = FMT == kPfNf3 ? 24 : 32;                 // code bytes per row per step
+  const uint8_t* qrow = (FMT == kPfNf3 ? a.nq : a.kq) + ((size_t)loc * a.rows_w + wrow) * RB +
+                        (FMT == kPfNf3 ? 12 : 16) * uu;
+  const uint8_t* s8row = a.ks + ((size_t)loc * a.rows_w + wrow) * (a.K / (FMT == kPfNvfp4 ? 16 : 32));
+  const uint16_t* s16row = a.ns + ((size_t)loc * a.rows_w + wrow) * (a.K / 64);
+  auto load_w = [&](int st, WRaw& w) {
+    if constexpr (FMT == kPfNf3) {
+      const uint3 v = *reinterpret_cast<const uint3*>(qrow + st * CB);
+      w.q = make_uint4(v.x, v.y, v.z, 0u);
+      w.s = s16row[st];
+    } else {
+      w.q = *reinterpret_cast<const uint4*>(qrow + st * CB);
+      if (FMT == kPfNvfp4) w.s = *reinterpret_cast<const uint16_t*>(s8row + 4 * st + 2 * uu);
+      else w.s = s8row[2 * st + uu];
+    }
+  };
 
-  // activation rows of this thread (16-byte piece c of row m), fixed over K
-  const uint16_t* arow[S::A_PER];
-  int apiece[S::A_PER];
+  // ---- per-row reference exponent (MXFP4: largest E8M0 byte; NF3: largest fp16
+  // exponent field of the row's group scales), the two threads of a row splitting it
+  int ref = 0;
+  if (FMT == kPfMxfp4) {
+    for (int i = uu; i < a.K / 32; i += 2) ref = max(ref, (int)s8row[i]);
+  } else if (FMT == kPfNf3) {
+    for (int i = uu; i < a.K / 64; i += 2) ref = max(ref, (int)((s16row[i] >> 10) & 0x1F));
+  }
+  if (FMT != kPfNvfp4) {
+    ref = max(ref, __shfl_xor(ref, 1));
+    if (uu == 0) sm.sRef[r] = ref;
+  }
+  if (FMT == kPfNf3) {
+    // thread t writes fields (t >> 5) + 8 i of column t & 31: low code t >> 5, high i
+    const float lo = nf3_level(tid >> 5) * kNF3TableScaleF16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sm.lut[((tid >> 5) + 8 * i) * 32 + (tid & 31)] =
+          pack_f16(lo, __uint_as_float(kNF3Bits[i]) * kNF3TableScaleF16);
+  }
+  const uint32_t* lut = sm.lut + (lane & 31);
+
+  // decodes one raw unit into the B stage: 16 fp16 pairs, four 16-byte chunks
+  auto store_w = [&](int buf, const WRaw& w) {
+    uint32_t v[16];
+    if constexpr (FMT == kPfNvfp4) {
+      nvfp4_block_f16(w.q.x, w.q.y, w.s & 0xFFu, v);
+      nvfp4_block_f16(w.q.z, w.q.w, (w.s >> 8) & 0xFFu, v + 8);
+    } else if constexpr (FMT == kPfMxfp4) {
+      const float so = e8m0_scale_operand((uint32_t)max((int)w.s - ref + 127, 0));
+      const uint32_t qq[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[4 * i + 0] = e2m1x2_f16<0>(qq[i], so);
+        v[4 * i + 1] = e2m1x2_f16<1>(qq[i], so);
+        v[4 * i + 2] = e2m1x2_f16<2>(qq[i], so);
+        v[4 * i + 3] = e2m1x2_f16<3>(qq[i], so);
+      }
+    } else {
+      const uint32_t d0 = w.q.x, d1 = w.q.y, d2 = w.q.z;
+      const _Float16 mu = (_Float16)__builtin_ldexpf(fp16_to_f32(w.s), 15 - ref);
+      const f16x2 m = {mu, mu};
+      v[0] = mul_f16x2(lut[nf3_pair_field<0>(d0, d1, d2) << 5], m);
+      v[1] = mul_f16x2(lut[nf3_pair_field<1>(d0, d1, d2) << 5], m);
+      v[2] = mul_f16x2(lut[nf3_pair_field<2>(d0, d1, d2) << 5], m);
+      v[3] = mul_f16x2(lut[nf3_pair_field<3>(d0, d1, d2) << 5], m);
+      v[4] = mul_f16x2(lut[nf3_pair_field<4>(d0, d1, d2) << 5], m);
+      v[5] = mul_f16x2(lut[nf3_pair_field<5>(d0, d1, d2) << 5], m);
+      v[6] = mul_f16x2(lut[nf3_pair_field<6>(d0, d1, d2) << 5], m);
+      v[7] = mul_f16x2(lut[nf3_pair_field<7>(d0, d1, d2) << 5], m);
+      v[8] = mul_f16x2(lut[nf3_pair_field<8>(d0, d1, d2) << 5], m);
+      v[9] = mul_f16x2(lut[nf3_pair_field<9>(d0, d1, d2) << 5], m);
+      v[10] = mul_f16x2(lut[nf3_pair_field<10>(d0, d1, d2) << 5], m);
+      v[11] = mul_f16x2(lut[nf3_pair_field<11>(d0, d1, d2) << 5], m);
+      v[12] = mul_f16x2(lut[nf3_pair_field<12>(d0, d1, d2) << 5], m);
+      v[13] = mul_f16x2(lut[nf3_pair_field<13>(d0, d1, d2) << 5], m);
+      v[14] = mul_f16x2(lut[nf3_pair_field<14>(d0, d1, d2) << 5], m);
+      v[15] = mul_f16x2(lut[nf3_pair_field<15>(d0, d1, d2) << 5], m);
+    }
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 0)]) = make_uint4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 1)]) = make_uint4(v[4], v[5], v[6], v[7]);
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 2)]) = make_uint4(v[8], v[9], v[10], v[11]);
+    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 3)]) = make_uint4(v[12], v[13], v[14], v[15]);
+  };
+
+  // ---- activation rows of this thread (16-byte piece pc of row m), fixed over K.
+  // Loads are unconditional (rows without a slot read row 0 and are zeroed on store)
+  // so the compiler can count outstanding loads exactly across the pipeline.
+  uint32_t aoff[S::A_PER];
+  uint32_t amask[S::A_PER];
 #pragma unroll
   for (int i = 0; i < S::A_PER; ++i) {
     const int c = tid + kPfThreads * i;
     const int m = c / (kBK / 8);
-    apiece[i] = c - m * (kBK / 8);
-    arow[i] = nullptr;
+    const int pc = c - m * (kBK / 8);
+    amask[i] = 0u;
+    aoff[i] = 0;
     if (c < S::A_CHUNKS) {
       if (W13) {
         const int slot = bslots[m];
-        if ((unsigned)slot < (unsigned)a.nslot) arow[i] = a.act + (size_t)(slot / a.k) * a.K;
+        if ((unsigned)slot < (unsigned)a.nslot) {
+          amask[i] = 0xFFFFFFFFu;
+          aoff[i] = (uint32_t)(slot / a.k) * a.K + 8 * pc;
+        }
       } else {
-        arow[i] = a.act + (hbase + m) * a.K;
+        amask[i] = 0xFFFFFFFFu;
+        aoff[i] = (uint32_t)((hbase + m) * a.K) + 8 * pc;
       }
     }
   }
-
-  if (FMT == kPfNf3) {
-    // thread t writes fields (t >> 5) + 8j of column t & 31: low code t >> 5, high j
-    const float lo = nf3_level(tid >> 5) * kNF3TableScaleF16;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      lut[((tid >> 5) + 8 * j) * 32 + (tid & 31)] =
-          pack_f16(lo, __uint_as_float(kNF3Bits[j]) * kNF3TableScaleF16);
-  }
-  if (FMT == kPfMxfp4) {
-    // largest E8M0 byte of each tile row over the whole K
-    for (int rr = wave; rr < kBN; rr += kPfThreads / kWave) {
-      int row;
-      if (W13) row = rr < kBN / 2 ? n0 + rr : a.I + n0 + (rr - kBN / 2);
-      else row = n0 + rr;
-      const uint8_t* srow = a.ks + ((size_t)loc * a.rows_w + row) * (a.K / 32);
-      int m = 0;
-      for (int i = lane; i < a.K / 32; i += kWave) m = max(m, (int)srow[i]);
-      m = max(m, __shfl_xor(m, 32));
-      m = max(m, __shfl_xor(m, 16));
-      m = max(m, __shfl_xor(m, 8));
-      m = max(m, __shfl_xor(m, 4));
-      m = max(m, __shfl_xor(m, 2));
-      m = max(m, __shfl_xor(m, 1));
-      if (lane == 0) sRef[rr] = m;
-    }
-  }
-
-  // registers of the step in flight
-  uint4 av[S::A_PER];
-  RawUnit wu;
-  auto load_step = [&](int st) {
-    const int k0 = st * kBK;
+  auto load_a = [&](int st, uint4 (&v)[S::A_PER]) {
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i)
-      av[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + 8 * apiece[i])
-                      : make_uint4(0u, 0u, 0u, 0u);
-    wu = load_unit<FMT>(a, grow, 2 * st + uu);
+      v[i] = *reinterpret_cast<const uint4*>(a.act + aoff[i] + st * kBK);
   };
-  auto store_step = [&](int buf, int ref) {
+  auto store_a = [&](int buf, const uint4 (&v)[S::A_PER]) {
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) {
       const int c = tid + kPfThreads * i;
       if (c < S::A_CHUNKS) {
         const int m = c / (kBK / 8);
-        *reinterpret_cast<uint4*>(&As[buf][m][swz(m, apiece[i])]) = av[i];
+        const uint32_t k = amask[i];
+        *reinterpret_cast<uint4*>(&As[buf][m][swz(m, c - m * (kBK / 8))]) =
+            make_uint4(v[i].x & k, v[i].y & k, v[i].z & k, v[i].w & k);
       }
     }
-    uint32_t w[16];
-    decode_unit<FMT>(wu, ref, lut + (lane & 31), w);
-    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 0)]) = make_uint4(w[0], w[1], w[2], w[3]);
-    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 1)]) = make_uint4(w[4], w[5], w[6], w[7]);
-    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 2)]) = make_uint4(w[8], w[9], w[10], w[11]);
-    *reinterpret_cast<uint4*>(&Bs[buf][r][swz(r, 4 * uu + 3)]) = make_uint4(w[12], w[13], w[14], w[15]);
-    if (FMT == kPfNf3 && uu == 0) sS[buf][r] = fp16_to_f32(wu.s);
   };
 
   f32x4 acc[MT][NT];
@@ -285,74 +281,97 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_step(0);
-  __syncthreads();  // table and reference bytes
-  const int ref = FMT == kPfMxfp4 ? sRef[r] : 0;
-  store_step(0, ref);
-  __syncthreads();
-
-  for (int st = 0; st < steps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < steps) load_step(st + 1);
-    f32x4 part[MT][NT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        part[mt][nt] = FMT == kPfNf3 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mt][nt];
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
-      // chunk 4 ks + lane / 16 of rows lane % 16 (row bases are multiples of 16)
-      const int kk = swz(lane, 4 * ks + (lane >> 4));
+      const int kk = swz(lane, 4 * ks + g);  // row bases are multiples of 16
       uint4 bq[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
-        bq[nt] = *reinterpret_cast<const uint4*>(&Bs[buf][tile_row<BM, W13>(wn, nt) + (lane & 15)][kk]);
+        bq[nt] = *reinterpret_cast<const uint4*>(&Bs[buf][tile_row<BM, W13>(wn, nt) + j][kk]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 aq = *reinterpret_cast<const uint4*>(&As[buf][(wm * MT + mt) * 16 + (lane & 15)][kk]);
+        const uint4 aq = *reinterpret_cast<const uint4*>(&As[buf][(wm * MT + mt) * 16 + j][kk]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          part[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              __builtin_bit_cast(f16x8, aq), __builtin_bit_cast(f16x8, bq[nt]), part[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8, aq), __builtin_bit_cast(f16x8, bq[nt]), acc[mt][nt], 0, 0, 0);
       }
     }
-    if constexpr (FMT == kPfNf3) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const float s = sS[buf][tile_row<BM, W13>(wn, nt) + (lane & 15)];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[mt][nt][q] = __builtin_fmaf(s, part[mt][nt][q], acc[mt][nt][q]);
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = part[mt][nt];
-    }
-    if (st + 1 < steps) store_step(buf ^ 1, ref);
+  };
+
+  // ---- pipeline. Raw weight units are loaded three steps ahead into a ring of four
+  // register slots and decoded into the free LDS stage one step ahead; activations
+  // are loaded two steps ahead into two register sets. Each step issues its loads in
+  // the order they are consumed (vector memory completes in order), and the stores
+  // of the next stage stay behind the MFMAs. The steady state runs unguarded in
+  // groups of four steps; the last steps run guarded.
+  WRaw wr0, wr1, wr2, wr3;
+  uint4 av0[S::A_PER], av1[S::A_PER];
+  load_a(0, av0);
+  load_w(0, wr0);
+  if (1 < steps) load_a(1, av1);
+  if (1 < steps) load_w(1, wr1);
+  if (2 < steps) load_w(2, wr2);
+  __syncthreads();  // table, reference exponents
+  store_a(0, av0);
+  store_w(0, wr0);
+  __syncthreads();
+  // step st: MFMAs on stage st & 1; stage (st + 1) & 1 takes activations cur and the
+  // raw weights next; loads fill nxt (activations of st + 2) and ahead (weights st + 3)
+  auto step_full = [&](int st, uint4 (&cur)[S::A_PER], uint4 (&nxt)[S::A_PER],
+                       const WRaw& next, WRaw& ahead) {
+    load_a(st + 2, nxt);
+    load_w(st + 3, ahead);
+    compute(st & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_a((st + 1) & 1, cur);
+    store_w((st + 1) & 1, next);
     __syncthreads();
+  };
+  auto step_tail = [&](int st, uint4 (&cur)[S::A_PER], uint4 (&nxt)[S::A_PER],
+                       const WRaw& next, WRaw& ahead) {
+    if (st + 2 < steps) load_a(st + 2, nxt);
+    if (st + 3 < steps) load_w(st + 3, ahead);
+    compute(st & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < steps) {
+      store_a((st + 1) & 1, cur);
+      store_w((st + 1) & 1, next);
+    }
+    __syncthreads();
+  };
+  int st = 0;
+  for (; st + 7 <= steps; st += 4) {  // steps st .. st + 3, loads up to st + 6
+    step_full(st, av1, av0, wr1, wr3);
+    step_full(st + 1, av0, av1, wr2, wr0);
+    step_full(st + 2, av1, av0, wr3, wr1);
+    step_full(st + 3, av0, av1, wr0, wr2);
+  }
+  for (; st < steps; st += 4) {
+    step_tail(st, av1, av0, wr1, wr3);
+    if (st + 1 < steps) step_tail(st + 1, av0, av1, wr2, wr0);
+    if (st + 2 < steps) step_tail(st + 2, av1, av0, wr3, wr1);
+    if (st + 3 < steps) step_tail(st + 3, av0, av1, wr0, wr2);
   }
 
-  // epilogue: lane holds rows 4 * (lane / 16) + q of each 16-row tile, column lane % 16
+  // ---- epilogue: lane holds rows 4 * g + q of each 16-row tile, column j
+  auto col_factor = [&](int trow) {
+    if (FMT == kPfNf3) return __builtin_ldexpf(1.0f / kNF3TableScaleF16, sm.sRef[trow] - 15);
+    if (FMT == kPfNvfp4) return a.kg[loc];
+    return e8m0_to_f32((uint32_t)sm.sRef[trow]);
+  };
 #pragma unroll
   for (int nt = 0; nt < (W13 ? NT / 2 : NT); ++nt) {
-    const int tr = tile_row<BM, W13>(wn, nt) + (lane & 15);   // gate / W2 tile row
-    auto col_factor = [&](int trow) {
-      if (FMT == kPfNf3) return 1.0f / kNF3TableScaleF16;
-      if (FMT == kPfNvfp4) return a.kg[loc];
-      return e8m0_to_f32((uint32_t)sRef[trow]);
-    };
+    const int tr = tile_row<BM, W13>(wn, nt) + j;
+    const int n = n0 + tr;
     const float gf = col_factor(tr);
-    const float uf = W13 ? col_factor(tile_row<BM, W13>(wn, nt + NT / 2) + (lane & 15)) : 0.0f;
-    const int n = n0 + (W13 ? tr : tr);
+    const float uf = W13 ? col_factor(tile_row<BM, W13>(wn, nt + NT / 2) + j) : 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int m = (wm * MT + mt) * 16 + 4 * (lane >> 4) + q;
+        const int m = (wm * MT + mt) * 16 + 4 * g + q;
         const int slot = bslots[m];
         if (W13) {
           // x was scaled by 2^-xe[token]
