@@ -166,10 +166,24 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
     stage_us = [sum(ev[i][st].elapsed_time(ev[i][st + 1]) for i in range(stage_steps)) * 1e3 / stage_steps
                 for st in range(4)]
 
+    # the dominant stage (W13) alone: back-to-back launches over the weight copies
+    # between two events on the launch stream; the average is one launch's duration
+    reps = max(30, stage_steps)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(1e8))
+    k0.record()
+    for i in range(reps):
+        hm.hybrid_moe_forward_stage(layer, wts[i % copies], x, lg, y, scratch, hm.STAGE_W13)
+    k1.record()
+    torch.cuda.synchronize()
+    w13_launch_us = k0.elapsed_time(k1) * 1e3 / reps
+
     # algorithmic work from the routing this batch produced
     eb = expert_bytes(packed)
     k, M = w.top_k, w.M
     res = {"ms_per_step": ms_per_step, "stage_us": stage_us, "copies": copies, "block_m": block_m,
+           "w13_launch_us": w13_launch_us,
            "layer_bytes_resident": layer_bytes, "desc": describe(w, packed)}
     io_bytes = M * w.H * 2 + M * w.E * 4 + M * w.H * 2        # x, logits, y
     if M <= hm.DECODE_MAX_M:
@@ -240,6 +254,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1,2,4 decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=None, metavar="MIB",
+                    help="only copy MIB mebibytes device to device five times (the plain copy "
+                         "the HBM traffic counters are scaled by) and exit")
     ap.add_argument("--block-m", type=int, default=None,
                     help="prefill GEMM rows per expert block (16/32/64/128; default 128)")
     args = ap.parse_args()
@@ -254,6 +271,17 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}))
+        return
     import weight_only_quantized_moe_amd as hm
     hm.load_library()
 
@@ -284,23 +312,23 @@ def main():
     }
     src = source_hash("decode.hip" if decode else "prefill.hip", "device_common.h")
     if decode:
-        t_w13 = r["stage_us"][1] * 1e-6
+        t_w13 = r["w13_launch_us"] * 1e-6
         achieved = r["w13_bytes"] / t_w13 / 1e9
         out["distinct_experts"] = r["distinct_experts"]
         out["roofline"] = {"bound": "hbm", "kernel": "gemv_kernel<W13> (decode W13 + SwiGLU)",
                            "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": achieved / HBM_PEAK_GBPS, "algorithmic_bytes": r["w13_bytes"],
-                           "avg_launch_us": r["stage_us"][1],
+                           "avg_launch_us": r["w13_launch_us"],
                            "traffic": pmc_traffic("decode_w13_" + w.name, src, r["w13_bytes"])}
         out["config"]["distinct_experts"] = r["distinct_experts"]
     else:
-        t_w13 = r["stage_us"][1] * 1e-6
+        t_w13 = r["w13_launch_us"] * 1e-6
         achieved = r["w13_flops"] / t_w13 / 1e12
         out["tflops"] = r["flops"] / (ms * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "kernel": "grouped_gemm_kernel<W13> (prefill W13 + SwiGLU)",
                            "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": r["w13_flops"],
-                           "avg_launch_us": r["stage_us"][1],
+                           "avg_launch_us": r["w13_launch_us"],
                            "traffic": pmc_traffic("prefill_w13_" + w.name, src, None)}
         out["config"]["touched_experts"] = r["touched_experts"]
         out["config"]["block_m"] = r["block_m"]
@@ -312,7 +340,7 @@ def main():
             sweep.append({"M": m, "tok_per_s": m / (rm["ms_per_step"] * 1e-3),
                           "ms_per_step": rm["ms_per_step"],
                           "hbm_gbps": rm["layer_bytes"] / (rm["ms_per_step"] * 1e-3) / 1e9,
-                          "w13_frac_of_hbm_peak": rm["w13_bytes"] / (rm["stage_us"][1] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                          "w13_frac_of_hbm_peak": rm["w13_bytes"] / (rm["w13_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
                           "distinct_experts": rm["distinct_experts"]})
         sweep.append({"M": w.M, "tok_per_s": out["value"], "ms_per_step": ms, "hbm_gbps": out["hbm_gbps"],
                       "w13_frac_of_hbm_peak": out["roofline"]["frac"], "distinct_experts": r["distinct_experts"]})

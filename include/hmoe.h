@@ -241,8 +241,8 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
 
 /* One stage of hybrid_moe_forward, for profiling: with the same arguments, calling
  * HMOE_STAGE_ROUTE, _W13, _W2 and _COMBINE in that order on one stream is exactly
- * hybrid_moe_forward. ROUTE is routing plus the decode grouping (M <= 8) or routing
- * plus the per-tier align (M > 8); W13 is the expert up projection with the fused
+ * hybrid_moe_forward. ROUTE is routing plus the decode grouping (M <= 8) or routing,
+ * the per-tier align and the tokens' conversion to scaled fp16 (M > 8); W13 is the expert up projection with the fused
  * SwiGLU; W2 the down projection with the routing weight; COMBINE the fixed-order
  * top-k sum into y. Each stage reads what the previous stages left in scratch, so a
  * stage run out of order computes from stale scratch contents (no fault, since every

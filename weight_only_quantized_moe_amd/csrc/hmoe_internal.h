@@ -77,6 +77,10 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
                           uint16_t* y, void* scratch, int stage, hipStream_t s);
 
+// prefill.hip: tokens to fp16 with a per-token power-of-two scale (prefill input)
+hipError_t launch_prefill_x16(const Layer& L, const uint16_t* x, int M, void* scratch,
+                              hipStream_t s);
+
 // dequant.hip
 hipError_t launch_dequant(const Layer& L, const hmoe_weights& W, int expert, int tensor,
                           float* out_f32, uint16_t* out_bf16, hipStream_t s);

@@ -317,6 +317,7 @@ hmoe_status hybrid_moe_forward_stage(const hmoe_layer* layer, const hmoe_weights
       err = hmoe::launch_route(router_logits, M, L.E, L.k, ids,
                                reinterpret_cast<float*>(b + L.plan.topk_w), stream);
       if (err == hipSuccess) err = hmoe::launch_align(L, ids, M, scratch, stream);
+      if (err == hipSuccess) err = hmoe::launch_prefill_x16(L, x, M, scratch, stream);
     }
   } else if (decode) {
     err = hmoe::launch_decode(L, *weights, x, M, y, scratch, stage, stream);

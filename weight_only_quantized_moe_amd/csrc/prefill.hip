@@ -453,6 +453,15 @@ static GemmFn pick_gemm(int bm) {
   return nullptr;
 }
 
+hipError_t launch_prefill_x16(const Layer& L, const uint16_t* x, int M, void* scratch,
+                              hipStream_t s) {
+  char* base = static_cast<char*>(scratch);
+  hipLaunchKernelGGL(prefill_x16_kernel, dim3(M), dim3(256), 0, s, x, L.H,
+                     reinterpret_cast<uint16_t*>(base + L.plan.x16_pre),
+                     reinterpret_cast<int32_t*>(base + L.plan.xe_pre));
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
                           uint16_t* y, void* scratch, int stage, hipStream_t s) {
   char* base = static_cast<char*>(scratch);
@@ -485,7 +494,6 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
   int32_t* xe = reinterpret_cast<int32_t*>(base + P.xe_pre);
   const int nblk = a.nblk0 + a.nblk1;
   if (stage == HMOE_STAGE_W13) {
-    hipLaunchKernelGGL(prefill_x16_kernel, dim3(M), dim3(256), 0, s, x, L.H, x16, xe);
     PrefillArgs b = a;
     b.kq = W.kept_w13_q; b.ks = W.kept_w13_s; b.kg = W.kept_w13_g;
     b.nq = W.nf3_w13_q; b.ns = W.nf3_w13_s;
