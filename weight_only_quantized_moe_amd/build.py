@@ -20,6 +20,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "route.hip", "align.hip", "decode.hip", "prefill.hip", "dequant.hip"]
+# the streaming kernels must keep every value in registers: private-memory (scratch)
+# traffic shares the vector memory counter with the prefetched loads and drains them
+NO_SCRATCH = {"decode.hip", "prefill.hip"}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -31,14 +34,27 @@ COMMON = [
 def _compile(src: str, obj_dir: str, verbose: bool) -> str:
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    check = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SCRATCH else []
+    cmd = [HIPCC, *COMMON, *lang, *check, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                     if "packed-fp32-ops" not in l)
+    lines = (r.stdout + r.stderr).splitlines()
+    msgs = "\n".join(l for l in lines
+                     if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+    if check:
+        kernel, spills = None, []
+        for l in lines:
+            if "Function Name:" in l:
+                kernel = l.split("Function Name:")[1].split("[")[0].strip()
+            elif "ScratchSize [bytes/lane]:" in l:
+                n = int(l.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+                if n:
+                    spills.append(f"{kernel}: {n} bytes/lane")
+        if spills:
+            raise RuntimeError(f"{src}: kernels use private memory:\n" + "\n".join(spills))
     if verbose and msgs.strip():
         print(msgs)
     return obj

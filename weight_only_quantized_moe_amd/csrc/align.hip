@@ -3,13 +3,16 @@
 // local-inference-lab/vllm PR #104: compact tier-local storage), ascending slot order
 // inside an expert, each expert's run padded with the sentinel M*k to a multiple of
 // block_m, plus the block -> expert table and the padded offsets. One block of 1024
-// threads; deterministic; no host read-back.
+// threads: each of its 16 waves places one contiguous chunk of the slots, starting
+// from per-wave, per-expert offsets, so the result is the stable order of a serial
+// counting sort. Deterministic; no host read-back.
 #include "device_common.h"
 #include "hmoe_internal.h"
 
 namespace hmoe {
 
 constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / kWave;
 
 struct AlignArgs {
   const int32_t* ids;
@@ -34,21 +37,27 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_off[kMaxExperts];
   __shared__ int32_t s_tc[kMaxExperts];
-  __shared__ int32_t s_run[kMaxExperts];
+  __shared__ int32_t s_w[kAlignWaves][kMaxExperts];  // per-wave counts, then positions
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
+  // wave w places slots [w * chunk, (w + 1) * chunk), chunk a multiple of 64
+  const int chunk = ((a.nslot + kAlignWaves * kWave - 1) / (kAlignWaves * kWave)) * kWave;
+  const int c0 = min(wave * chunk, a.nslot), c1 = min(c0 + chunk, a.nslot);
   for (int e = tid; e < a.E; e += kAlignThreads) {
     const int32_t tc = tier_code_a(tm, e);
     s_tc[e] = tc;
     s_cnt[e] = 0;
-    s_run[e] = 0;
     a.expert_tier[e] = tc;
   }
+  for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&s_w[0][0])[i] = 0;
   __syncthreads();
-  for (int s = tid; s < a.nslot; s += kAlignThreads) {
+  for (int s = c0 + lane; s < c1; s += kWave) {
     const int e = a.ids[s];
-    if ((unsigned)e < (unsigned)a.E) atomicAdd(&s_cnt[e], 1);  // ids outside [0, E) are dropped
+    if ((unsigned)e < (unsigned)a.E) {  // ids outside [0, E) are dropped
+      atomicAdd(&s_cnt[e], 1);
+      atomicAdd(&s_w[wave][e], 1);
+    }
   }
   __syncthreads();
   // padded exclusive offsets, one wave per tier, experts in ascending id
@@ -80,7 +89,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
     }
   }
   __syncthreads();
-  // block -> expert table and sentinel padding, one thread per expert
+  // block -> expert table and sentinel padding, one thread per expert; the per-wave
+  // counts become each wave's first position for that expert
   for (int e = tid; e < a.E; e += kAlignThreads) {
     const int t = s_tc[e] >> 16;
     const int loc = s_tc[e] & 0xFFFF;
@@ -89,35 +99,41 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
     const int off = s_off[e];
     for (int b = off / a.bm; b < (off + padded) / a.bm; ++b) a.bexp[t][b] = loc;
     for (int p = off + n; p < off + padded; ++p) a.slots[t][p] = a.nslot;
-  }
-  // real slots in ascending order: one wave walks the slots 64 at a time, ranking
-  // equal experts inside the step with ballots
-  if (wave == 0) {
-    for (int base = 0; base < a.nslot; base += kWave) {
-      const int s = base + lane;
-      const int e0 = s < a.nslot ? a.ids[s] : -1;
-      const bool valid = (unsigned)e0 < (unsigned)a.E;
-      const int e = valid ? e0 : 0;
-      uint64_t m = __ballot(valid);
-#pragma unroll
-      for (int b = 0; b < 10; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t bb = __ballot(bit);
-        m &= bit ? bb : ~bb;
-      }
-      const int rank = __popcll(m & ((1ull << lane) - 1ull));
-      const int cnt = __popcll(m);
-      int pos = 0;
-      if (valid) pos = s_off[e] + s_run[e] + rank;
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0);
-      if (valid) {
-        a.slots[s_tc[e] >> 16][pos] = s;
-        if (rank == cnt - 1) s_run[e] += cnt;
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_s_waitcnt(0);
+    int run = off;
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int c = s_w[w][e];
+      s_w[w][e] = run;
+      run += c;
     }
+  }
+  __syncthreads();
+  // real slots in ascending order inside each wave's chunk: 64 at a time, ranking
+  // equal experts inside the step with ballots over the id bits
+  int idbits = 1;
+  while ((1 << idbits) < a.E) ++idbits;
+  for (int base = c0; base < c1; base += kWave) {
+    const int s = base + lane;
+    const int e0 = s < c1 ? a.ids[s] : -1;
+    const bool valid = (unsigned)e0 < (unsigned)a.E;
+    const int e = valid ? e0 : 0;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < idbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    const int cnt = __popcll(m);
+    int pos = 0;
+    if (valid) pos = s_w[wave][e] + rank;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
+    if (valid) {
+      a.slots[s_tc[e] >> 16][pos] = s;
+      if (rank == cnt - 1) s_w[wave][e] += cnt;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0);
   }
 }
 

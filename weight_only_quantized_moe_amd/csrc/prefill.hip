@@ -233,26 +233,22 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   };
 
   // ---- activation rows of this thread (16-byte piece pc of row m), fixed over K.
-  // Loads are unconditional (rows without a slot read row 0 and are zeroed on store)
-  // so the compiler can count outstanding loads exactly across the pipeline.
+  // Padding rows (no slot) read row 0: a GEMM never mixes rows, their outputs are
+  // never used (W13's h rows of padding only feed W2's padding rows, whose outputs
+  // the epilogue drops), and unconditional loads let the compiler count outstanding
+  // loads exactly across the pipeline.
   uint32_t aoff[S::A_PER];
-  uint32_t amask[S::A_PER];
 #pragma unroll
   for (int i = 0; i < S::A_PER; ++i) {
     const int c = tid + kPfThreads * i;
     const int m = c / (kBK / 8);
     const int pc = c - m * (kBK / 8);
-    amask[i] = 0u;
     aoff[i] = 0;
     if (c < S::A_CHUNKS) {
       if (W13) {
         const int slot = bslots[m];
-        if ((unsigned)slot < (unsigned)a.nslot) {
-          amask[i] = 0xFFFFFFFFu;
-          aoff[i] = (uint32_t)(slot / a.k) * a.K + 8 * pc;
-        }
+        if ((unsigned)slot < (unsigned)a.nslot) aoff[i] = (uint32_t)(slot / a.k) * a.K + 8 * pc;
       } else {
-        amask[i] = 0xFFFFFFFFu;
         aoff[i] = (uint32_t)((hbase + m) * a.K) + 8 * pc;
       }
     }
@@ -268,9 +264,10 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
       const int c = tid + kPfThreads * i;
       if (c < S::A_CHUNKS) {
         const int m = c / (kBK / 8);
-        const uint32_t k = amask[i];
+        // per-component copy: a whole-vector copy out of the register set makes the
+        // compiler keep the sets in private memory
         *reinterpret_cast<uint4*>(&As[buf][m][swz(m, c - m * (kBK / 8))]) =
-            make_uint4(v[i].x & k, v[i].y & k, v[i].z & k, v[i].w & k);
+            make_uint4(v[i].x, v[i].y, v[i].z, v[i].w);
       }
     }
   };
