@@ -638,10 +638,10 @@ static GemvFn pick_gemv(const GemvTiling& t) {
     if constexpr (W13) return w13_gemv_kernel<LR_, KU_, RI_>;                   \
     else return w2_gemv_kernel<LR_, KU_, RI_>;                                  \
   }
-  HMOE_GEMV_CASE(64, 1, 4) HMOE_GEMV_CASE(64, 2, 2) HMOE_GEMV_CASE(64, 3, 1) HMOE_GEMV_CASE(64, 4, 1)
-  HMOE_GEMV_CASE(32, 1, 4) HMOE_GEMV_CASE(32, 2, 2) HMOE_GEMV_CASE(32, 3, 1) HMOE_GEMV_CASE(32, 4, 1)
-  HMOE_GEMV_CASE(16, 1, 4) HMOE_GEMV_CASE(16, 2, 2) HMOE_GEMV_CASE(16, 3, 1) HMOE_GEMV_CASE(16, 4, 1)
-  HMOE_GEMV_CASE(8, 1, 4) HMOE_GEMV_CASE(8, 2, 2) HMOE_GEMV_CASE(8, 3, 1) HMOE_GEMV_CASE(8, 4, 1)
+  HMOE_GEMV_CASE(64, 1, 2) HMOE_GEMV_CASE(64, 2, 2) HMOE_GEMV_CASE(64, 3, 1) HMOE_GEMV_CASE(64, 4, 1)
+  HMOE_GEMV_CASE(32, 1, 2) HMOE_GEMV_CASE(32, 2, 2) HMOE_GEMV_CASE(32, 3, 1) HMOE_GEMV_CASE(32, 4, 1)
+  HMOE_GEMV_CASE(16, 1, 2) HMOE_GEMV_CASE(16, 2, 2) HMOE_GEMV_CASE(16, 3, 1) HMOE_GEMV_CASE(16, 4, 1)
+  HMOE_GEMV_CASE(8, 1, 2) HMOE_GEMV_CASE(8, 2, 2) HMOE_GEMV_CASE(8, 3, 1) HMOE_GEMV_CASE(8, 4, 1)
   HMOE_GEMV_CASE(4, 1, 2) HMOE_GEMV_CASE(4, 2, 2) HMOE_GEMV_CASE(4, 3, 1) HMOE_GEMV_CASE(4, 4, 1)
 #undef HMOE_GEMV_CASE
   return nullptr;
@@ -657,7 +657,7 @@ bool plan_gemv(int K, GemvTiling* t) {
   while (lr < 64 && U % (2 * lr) == 0) lr *= 2;
   const int ku = U / lr;
   if (lr < 4 || ku < 1 || ku > 4) return false;
-  int ri = ku == 1 ? 4 : (ku == 2 ? 2 : 1);
+  int ri = ku <= 2 ? 2 : 1;  // two row (pair) groups at most: three waves per SIMD fit
   while (ri * 2 > lr) ri /= 2;
   if (ri < 1) return false;
   t->lr = lr;
