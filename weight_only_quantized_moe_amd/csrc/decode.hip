@@ -280,10 +280,14 @@ struct WaveRange {
   int begin, end;
 };
 
+// WAVE_MAJOR numbers the runs wave index first, so the waves of one block (one CU)
+// take runs spread over the pass list and share each SIMD between both tiers' costs.
+template <bool WAVE_MAJOR>
 __device__ __forceinline__ WaveRange wave_range(int total) {
   const int nw = gridDim.x * kGemvWaves;
   // wave-uniform (scalar) from here on: the range, the pass, its tier and slot
-  const int gw = blockIdx.x * kGemvWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = WAVE_MAJOR ? wv * gridDim.x + blockIdx.x : blockIdx.x * kGemvWaves + wv;
   return {(int)((long)gw * total / nw), (int)((long)(gw + 1) * total / nw)};
 }
 
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
   constexpr int CH = (kWave / LR) * RI;  // pairs per chunk
   const uint32_t* lut_lane = lut + (threadIdx.x & (kWave - 1));
   const int per = a.out_units / CH;      // chunks per pass
-  const WaveRange wr = wave_range(a.npass * per);
+  const WaveRange wr = wave_range<false>(a.npass * per);
   // the first chunk's weights are requested before the table is built
   W13Buf<KU, RI> A, B;
   PassInfo pi{};
@@ -564,7 +568,7 @@ __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
   const uint32_t* lut_lane = lut + (threadIdx.x & (kWave - 1));
   uint32_t* hs = h_stage + KD * (threadIdx.x >> 6);
   const int per = a.out_units / CH;
-  const WaveRange wr = wave_range(a.npass * per);
+  const WaveRange wr = wave_range<true>(a.npass * per);
   W2Buf<KU, RI> A, B;
   PassInfo pi{};
   int4 r_first{}, r_next{};
