@@ -177,8 +177,8 @@ typedef struct hmoe_decode_view {
  * a bit map value other than 3 or 4, an unknown kept format or block_m);
  * HMOE_ERR_UNSUPPORTED (E > 1024, k > 16, H or I not a multiple of 128, a K for
  * which no decode tiling exists, max_tokens * top_k > 2^24, max_tokens * H or the
- * prefill h rows * I reaching 2^31, or more than 65535 prefill expert blocks of
- * block_m rows at max_tokens). */
+ * prefill h rows * I reaching 2^31, or a prefill GEMM grid of 2^31 blocks or more
+ * at max_tokens). */
 hmoe_status moe_layer_create(const hmoe_layer_desc* desc, hmoe_layer** out);
 
 /* Frees the handle's host memory. NULL is a no-op. */

@@ -176,11 +176,13 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
     delete h;
     return fail(HMOE_ERR_UNSUPPORTED, "max_tokens too large for this layer's prefill buffers");
   }
-  // the prefill GEMMs put the expert blocks of both tiers on the grid's y axis
-  if ((long)(L.cap[0] + L.cap[1]) / L.block_m > 65535) {
+  // the prefill GEMMs run (expert blocks of both tiers, rounded up to 64) x (column
+  // tiles) blocks on a 1-D grid
+  if (((long)(L.cap[0] + L.cap[1]) / L.block_m + 64) * std::max(L.I / 64, L.H / 128) >=
+      (1L << 31)) {
     delete h;
-    return fail(HMOE_ERR_UNSUPPORTED, "max_tokens * top_k / block_m too large (more than "
-                                      "65535 expert blocks): use a larger block_m");
+    return fail(HMOE_ERR_UNSUPPORTED, "max_tokens * top_k / block_m too large for the prefill "
+                                      "grid: use a larger block_m");
   }
   const bool tiled = hmoe::plan_gemv(L.H, &L.w13) && hmoe::plan_gemv(L.I, &L.w2) &&
                      L.I % ((64 / L.w13.lr) * L.w13.ri) == 0 && L.H % ((64 / L.w2.lr) * L.w2.ri) == 0;

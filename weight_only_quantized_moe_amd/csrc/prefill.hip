@@ -24,6 +24,9 @@
 //   NF3: the 64-entry table holds scaled level pairs (kNF3TableScaleF16); each K step
 //       is one group, so its two MFMAs accumulate into a fresh fp32 partial that is
 //       multiplied by the group's fp16 scale before it joins the accumulator.
+#include <type_traits>
+#include <utility>
+
 #include "device_common.h"
 #include "hmoe_internal.h"
 
@@ -35,6 +38,20 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kPfThreads = 256;
 constexpr int kBK = 64;         // K per step (one NF3 group)
 constexpr int kBN = 128;        // weight rows per tile
+constexpr int kWeightAhead = 4; // steps between a weight load and its decode
+constexpr int kActAhead = 2;    // steps between an activation load and its LDS store
+constexpr int kPipeGroup = 4;   // unrolled steps (a multiple of both distances and 2)
+constexpr int kXcdGroup = 1;    // expert blocks per XCD assignment unit
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<0>) ... f(integral_constant<N - 1>), in order
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // LDS tiles hold rows of 64 16-bit values (eight 16-byte chunks) with chunk c of row
 // r stored at chunk c ^ (r & 7): the 16-byte MFMA operand reads of 16 consecutive
@@ -58,6 +75,7 @@ struct PrefillArgs {
   const int32_t* npad[2];
   int nblk0;   // block count of tier 0 in this launch (tier 1 blocks follow)
   int nblk1;
+  int ntile;   // column tiles per expert block
   int E4, E3;
   int hrow1;   // h row of tier 1's first block
   int I, H;
@@ -130,7 +148,7 @@ __device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32
 }
 
 template <int BM, bool W13, int FMT>
-__device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b, int loc,
+__device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b, int loc, int tile,
                                           GemmSmem<BM>& sm) {
   using S = GemmShape<BM, W13>;
   constexpr int MT = S::MT, NT = S::NT;
@@ -141,7 +159,7 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   const int wave = tid >> 6;
   const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
   const int j = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * (W13 ? kBN / 2 : kBN);
+  const int n0 = tile * (W13 ? kBN / 2 : kBN);
   const int32_t* bslots = a.slots[tier] + (size_t)b * BM;
   const size_t hbase = (size_t)(tier ? a.hrow1 : 0) + (size_t)b * BM;
   const int steps = a.K / kBK;
@@ -262,7 +280,7 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
 #pragma unroll
     for (int i = 0; i < S::A_PER; ++i) {
       const int c = tid + kPfThreads * i;
-      if (c < S::A_CHUNKS) {
+      if (S::A_CHUNKS % kPfThreads == 0 || c < S::A_CHUNKS) {
         const int m = c / (kBK / 8);
         // per-component copy: a whole-vector copy out of the register set makes the
         // compiler keep the sets in private memory
@@ -297,59 +315,60 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
     }
   };
 
-  // ---- pipeline. Raw weight units are loaded three steps ahead into a ring of four
+  // ---- pipeline. Raw weight units are loaded WD steps ahead into a ring of WD
   // register slots and decoded into the free LDS stage one step ahead; activations
-  // are loaded two steps ahead into two register sets. Each step issues its loads in
+  // are loaded AD steps ahead into AD register sets. Step s uses weight slot s % WD
+  // and activation set s % AD, so a group of U steps (a multiple of WD, AD and the
+  // two LDS stages) names every slot at compile time. Each step issues its loads in
   // the order they are consumed (vector memory completes in order), and the stores
-  // of the next stage stay behind the MFMAs. The steady state runs unguarded in
-  // groups of four steps; the last steps run guarded.
-  WRaw wr0, wr1, wr2, wr3;
-  uint4 av0[S::A_PER], av1[S::A_PER];
-  load_a(0, av0);
-  load_w(0, wr0);
-  if (1 < steps) load_a(1, av1);
-  if (1 < steps) load_w(1, wr1);
-  if (2 < steps) load_w(2, wr2);
+  // of the next stage stay behind the MFMAs. Whole groups run unguarded; the last
+  // steps run guarded.
+  constexpr int WD = kWeightAhead, AD = kActAhead, U = kPipeGroup;
+  static_assert(U % WD == 0 && U % AD == 0 && U % 2 == 0, "pipeline group");
+  WRaw wr[WD];
+  uint4 av[AD][S::A_PER];
+  static_for<AD>([&](auto i) {
+    if (i.value < steps) load_a(i.value, av[i.value]);
+  });
+  static_for<WD>([&](auto i) {
+    if (i.value < steps) load_w(i.value, wr[i.value]);
+  });
   __syncthreads();  // table, reference exponents
-  store_a(0, av0);
-  store_w(0, wr0);
+  store_a(0, av[0]);
+  store_w(0, wr[0]);
   __syncthreads();
-  // step st: MFMAs on stage st & 1; stage (st + 1) & 1 takes activations cur and the
-  // raw weights next; loads fill nxt (activations of st + 2) and ahead (weights st + 3)
-  auto step_full = [&](int st, uint4 (&cur)[S::A_PER], uint4 (&nxt)[S::A_PER],
-                       const WRaw& next, WRaw& ahead) {
-    load_a(st + 2, nxt);
-    load_w(st + 3, ahead);
-    compute(st & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    store_a((st + 1) & 1, cur);
-    store_w((st + 1) & 1, next);
-    __syncthreads();
-  };
-  auto step_tail = [&](int st, uint4 (&cur)[S::A_PER], uint4 (&nxt)[S::A_PER],
-                       const WRaw& next, WRaw& ahead) {
-    if (st + 2 < steps) load_a(st + 2, nxt);
-    if (st + 3 < steps) load_w(st + 3, ahead);
-    compute(st & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if (st + 1 < steps) {
-      store_a((st + 1) & 1, cur);
-      store_w((st + 1) & 1, next);
-    }
-    __syncthreads();
-  };
+  // step st = group base + i: MFMAs on stage i & 1; stage (i + 1) & 1 takes the
+  // activations and raw weights of step st + 1; loads fill the activation set of
+  // st + AD and the weight slot of st + WD
   int st = 0;
-  for (; st + 7 <= steps; st += 4) {  // steps st .. st + 3, loads up to st + 6
-    step_full(st, av1, av0, wr1, wr3);
-    step_full(st + 1, av0, av1, wr2, wr0);
-    step_full(st + 2, av1, av0, wr3, wr1);
-    step_full(st + 3, av0, av1, wr0, wr2);
+  for (; st + U + WD <= steps; st += U) {
+    static_for<U>([&](auto I) {
+      constexpr int i = I.value;
+      load_a(st + i + AD, av[i % AD]);
+      load_w(st + i + WD, wr[i % WD]);
+      compute(i & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      store_a((i + 1) & 1, av[(i + 1) % AD]);
+      store_w((i + 1) & 1, wr[(i + 1) % WD]);
+      __syncthreads();
+    });
   }
-  for (; st < steps; st += 4) {
-    step_tail(st, av1, av0, wr1, wr3);
-    if (st + 1 < steps) step_tail(st + 1, av0, av1, wr2, wr0);
-    if (st + 2 < steps) step_tail(st + 2, av1, av0, wr3, wr1);
-    if (st + 3 < steps) step_tail(st + 3, av0, av1, wr0, wr2);
+  for (; st < steps; st += U) {
+    static_for<U>([&](auto I) {
+      constexpr int i = I.value;
+      const int s = st + i;
+      if (s < steps) {
+        if (s + AD < steps) load_a(s + AD, av[i % AD]);
+        if (s + WD < steps) load_w(s + WD, wr[i % WD]);
+        compute(i & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < steps) {
+          store_a((i + 1) & 1, av[(i + 1) % AD]);
+          store_w((i + 1) & 1, wr[(i + 1) % WD]);
+        }
+        __syncthreads();
+      }
+    });
   }
 
   // ---- epilogue: lane holds rows 4 * g + q of each 16-row tile, column j
@@ -388,9 +407,19 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
 
 template <int BM, bool W13>
 __global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs a) {
-  // blockIdx.x walks the output columns of one expert block, so the blocks that run
-  // together share its activation rows in cache and stream adjacent weight rows
-  const int by = blockIdx.y;
+  // A 1-D grid. The dispatcher hands consecutive block ids to the eight XCDs in
+  // turn (id L runs on XCD L % 8), so id L is given a group of kXcdGroup expert blocks
+  // owned by XCD L % 8, and the ids of one XCD walk a group's column tiles with its
+  // blocks innermost: an expert block's activation rows and the weight tile its
+  // group's blocks share stay in that XCD's L2.
+  const int L = blockIdx.x;
+  const int idx = L >> 3;
+  const int per_group = a.ntile * kXcdGroup;
+  const int grp = idx / per_group;
+  const int rem = idx - grp * per_group;
+  const int tile = rem / kXcdGroup;
+  const int by = (grp * 8 + (L & 7)) * kXcdGroup + (rem - tile * kXcdGroup);
+  if (by >= a.nblk0 + a.nblk1) return;
   const int tier = by < a.nblk0 ? 0 : 1;
   const int b = tier ? by - a.nblk0 : by;
   // npad and the block table come from the align stage; clamp to this launch's grid
@@ -399,9 +428,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs
   const int loc = a.bexp[tier][b];
   if ((unsigned)loc >= (unsigned)(tier ? a.E3 : a.E4)) return;
   __shared__ GemmSmem<BM> sm;
-  if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3>(a, tier, b, loc, sm);
-  else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4>(a, tier, b, loc, sm);
-  else gemm_tile<BM, W13, kPfMxfp4>(a, tier, b, loc, sm);
+  if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3>(a, tier, b, loc, tile, sm);
+  else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4>(a, tier, b, loc, tile, sm);
+  else gemm_tile<BM, W13, kPfMxfp4>(a, tier, b, loc, tile, sm);
 }
 
 // x16[t] = fp16(x[t] * 2^-e[t]), e[t] putting the token's largest |x| in [2^14, 2^15)
@@ -448,6 +477,12 @@ static GemmFn pick_gemm(int bm) {
     case 128: return grouped_gemm_kernel<128, W13>;
   }
   return nullptr;
+}
+
+// blocks of the 1-D GEMM grid: whole XCD groups of expert blocks times column tiles
+static unsigned gemm_grid(int nblk, int ntile) {
+  const int unit = 8 * kXcdGroup;
+  return (unsigned)((nblk + unit - 1) / unit * unit) * (unsigned)ntile;
 }
 
 hipError_t launch_prefill_x16(const Layer& L, const uint16_t* x, int M, void* scratch,
@@ -499,9 +534,10 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     b.act = x16;
     b.xe = xe;
     b.h_out = h;
+    b.ntile = L.I / (kBN / 2);
     GemmFn fn = pick_gemm<true>(bm);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(L.I / (kBN / 2), nblk), dim3(kPfThreads), 0, s, b);
+    hipLaunchKernelGGL(fn, dim3(gemm_grid(nblk, b.ntile)), dim3(kPfThreads), 0, s, b);
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_W2) {
@@ -513,9 +549,10 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     c.act = h;
     c.o_out = o;
     c.topk_w = w;
+    c.ntile = L.H / kBN;
     GemmFn fn = pick_gemm<false>(bm);
     if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(L.H / kBN, nblk), dim3(kPfThreads), 0, s, c);
+    hipLaunchKernelGGL(fn, dim3(gemm_grid(nblk, c.ntile)), dim3(kPfThreads), 0, s, c);
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_COMBINE) {
