@@ -40,7 +40,7 @@ constexpr int kBK = 64;         // K per step (one NF3 group)
 constexpr int kBN = 128;        // weight rows per tile
 constexpr int kWeightAhead = 4; // steps between a weight load and its decode
 constexpr int kActAhead = 2;    // steps between an activation load and its LDS store
-constexpr int kPipeGroup = 4;   // unrolled steps (a multiple of both distances and 2)
+constexpr int kPipeGroup = 8;   // unrolled steps (a multiple of both distances, 2 and 8)
 constexpr int kXcdGroup = 1;    // expert blocks per XCD assignment unit
 
 template <typename F, int... I>
@@ -76,6 +76,7 @@ struct PrefillArgs {
   int nblk0;   // block count of tier 0 in this launch (tier 1 blocks follow)
   int nblk1;
   int ntile;   // column tiles per expert block
+  int vec_scales;  // weight scale rows hold whole 16-byte vectors of 8 steps (K % 512 == 0)
   int E4, E3;
   int hrow1;   // h row of tier 1's first block
   int I, H;
@@ -147,7 +148,9 @@ __device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32
   w[7] = mul_f16x2(e2m1x2_f16<3>(q1, s), m);
 }
 
-template <int BM, bool W13, int FMT>
+// VS: the weight scales of 8 consecutive steps of a row are one aligned 16-byte vector
+// (two for NVFP4) and are loaded 8 steps at a time; otherwise one load per step.
+template <int BM, bool W13, int FMT, bool VS>
 __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b, int loc, int tile,
                                           GemmSmem<BM>& sm) {
   using S = GemmShape<BM, W13>;
@@ -173,24 +176,72 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
                         (FMT == kPfNf3 ? 12 : 16) * uu;
   const uint8_t* s8row = a.ks + ((size_t)loc * a.rows_w + wrow) * (a.K / (FMT == kPfNvfp4 ? 16 : 32));
   const uint16_t* s16row = a.ns + ((size_t)loc * a.rows_w + wrow) * (a.K / 64);
-  auto load_w = [&](int st, WRaw& w) {
+  // codes of step st; the scale word comes from load_s (one load per step) or from a
+  // vector of 8 steps' scales (VS)
+  auto load_q = [&](int st, WRaw& w) {
     if constexpr (FMT == kPfNf3) {
       const uint3 v = *reinterpret_cast<const uint3*>(qrow + st * CB);
       w.q = make_uint4(v.x, v.y, v.z, 0u);
-      w.s = s16row[st];
     } else {
       w.q = *reinterpret_cast<const uint4*>(qrow + st * CB);
-      if (FMT == kPfNvfp4) w.s = *reinterpret_cast<const uint16_t*>(s8row + 4 * st + 2 * uu);
-      else w.s = s8row[2 * st + uu];
     }
+  };
+  auto load_s = [&](int st) -> uint32_t {
+    if constexpr (FMT == kPfNf3) return s16row[st];
+    else if constexpr (FMT == kPfNvfp4) return *reinterpret_cast<const uint16_t*>(s8row + 4 * st + 2 * uu);
+    else return s8row[2 * st + uu];
+  };
+  constexpr int SG = 8;                         // steps per scale vector
+  constexpr int SW = FMT == kPfNvfp4 ? 8 : 4;   // dwords per scale vector
+  typedef uint32_t SVec[SW];
+  auto load_sv = [&](int grp, SVec& v) {
+    const uint4* p = FMT == kPfNf3 ? reinterpret_cast<const uint4*>(s16row + SG * grp)
+                                   : reinterpret_cast<const uint4*>(s8row + (FMT == kPfNvfp4 ? 4 : 2) * SG * grp);
+    const uint4 v0 = p[0];
+    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+    if constexpr (FMT == kPfNvfp4) {
+      const uint4 v1 = p[1];
+      v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+    }
+  };
+  // scale word of step SI (0..7) of a vector, for this thread's half of the row
+  auto scale_of = [&](const SVec& v, auto si) -> uint32_t {
+    constexpr int t = decltype(si)::value;
+    if constexpr (FMT == kPfNvfp4) return __builtin_amdgcn_ubfe(v[t], 16 * uu, 16);
+    else if constexpr (FMT == kPfMxfp4) return __builtin_amdgcn_ubfe(v[t >> 1], 16 * (t & 1) + 8 * uu, 8);
+    else return __builtin_amdgcn_ubfe(v[t >> 1], 16 * (t & 1), 16);
   };
 
   // ---- per-row reference exponent (MXFP4: largest E8M0 byte; NF3: largest fp16
-  // exponent field of the row's group scales), the two threads of a row splitting it
+  // exponent field of the row's group scales), the two threads of a row splitting it;
+  // the loads of a thread's share are independent, so they are issued together
   int ref = 0;
-  if (FMT == kPfMxfp4) {
+  if constexpr (FMT != kPfNvfp4 && VS) {
+    const uint4* p = FMT == kPfNf3 ? reinterpret_cast<const uint4*>(s16row)
+                                   : reinterpret_cast<const uint4*>(s8row);
+    const int nv = steps / SG;  // 16-byte vectors per row
+#pragma unroll 4
+    for (int c = uu; c < nv; c += 2) {
+      const uint4 v = p[c];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (FMT == kPfMxfp4) {
+          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 0, 8));
+          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 8, 8));
+          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 16, 8));
+          ref = max(ref, (int)(d[e] >> 24));
+        } else {
+          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 10, 5));
+          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 26, 5));
+        }
+      }
+    }
+  } else if constexpr (FMT == kPfMxfp4) {
+#pragma unroll 8
     for (int i = uu; i < a.K / 32; i += 2) ref = max(ref, (int)s8row[i]);
-  } else if (FMT == kPfNf3) {
+  } else if constexpr (FMT == kPfNf3) {
+#pragma unroll 8
     for (int i = uu; i < a.K / 64; i += 2) ref = max(ref, (int)((s16row[i] >> 10) & 0x1F));
   }
   if (FMT != kPfNvfp4) {
@@ -324,14 +375,21 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   // of the next stage stay behind the MFMAs. Whole groups run unguarded; the last
   // steps run guarded.
   constexpr int WD = kWeightAhead, AD = kActAhead, U = kPipeGroup;
-  static_assert(U % WD == 0 && U % AD == 0 && U % 2 == 0, "pipeline group");
+  static_assert(U % WD == 0 && U % AD == 0 && U % 2 == 0 && U % SG == 0 && WD <= SG,
+                "pipeline group");
   WRaw wr[WD];
   uint4 av[AD][S::A_PER];
+  SVec scur = {}, snext = {};  // VS: scale vectors of the current and the next group of SG steps
+  if constexpr (VS) load_sv(0, scur);
   static_for<AD>([&](auto i) {
     if (i.value < steps) load_a(i.value, av[i.value]);
   });
   static_for<WD>([&](auto i) {
-    if (i.value < steps) load_w(i.value, wr[i.value]);
+    if (i.value < steps) {
+      load_q(i.value, wr[i.value]);
+      if constexpr (VS) wr[i.value].s = scale_of(scur, i);
+      else wr[i.value].s = load_s(i.value);
+    }
   });
   __syncthreads();  // table, reference exponents
   store_a(0, av[0]);
@@ -339,35 +397,44 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   __syncthreads();
   // step st = group base + i: MFMAs on stage i & 1; stage (i + 1) & 1 takes the
   // activations and raw weights of step st + 1; loads fill the activation set of
-  // st + AD and the weight slot of st + WD
-  int st = 0;
-  for (; st + U + WD <= steps; st += U) {
-    static_for<U>([&](auto I) {
-      constexpr int i = I.value;
-      load_a(st + i + AD, av[i % AD]);
-      load_w(st + i + WD, wr[i % WD]);
-      compute(i & 1);
-      __builtin_amdgcn_sched_barrier(0);
+  // st + AD and the weight slot of st + WD (its scale from the current group's vector,
+  // or the next one's, requested at the group's first step)
+  auto step = [&](int st0, auto I, bool guarded) {
+    constexpr int i = I.value;
+    const int s = st0 + i;
+    if constexpr (VS && i % SG == 0) {
+      if (!guarded || s + SG < steps) load_sv((s + SG) / SG, snext);
+    }
+    if (!guarded || s + AD < steps) load_a(s + AD, av[(i + AD) % AD]);
+    if (!guarded || s + WD < steps) {
+      load_q(s + WD, wr[i % WD]);
+      if constexpr (VS) {
+        constexpr int t = (i + WD) % SG;
+        if constexpr ((i % SG) + WD < SG) wr[i % WD].s = scale_of(scur, std::integral_constant<int, t>{});
+        else wr[i % WD].s = scale_of(snext, std::integral_constant<int, t>{});
+      } else {
+        wr[i % WD].s = load_s(s + WD);
+      }
+    }
+    compute(i & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!guarded || s + 1 < steps) {
       store_a((i + 1) & 1, av[(i + 1) % AD]);
       store_w((i + 1) & 1, wr[(i + 1) % WD]);
-      __syncthreads();
-    });
+    }
+    __syncthreads();
+    if constexpr (VS && i % SG == SG - 1) {
+#pragma unroll
+      for (int e = 0; e < SW; ++e) scur[e] = snext[e];
+    }
+  };
+  int st = 0;
+  for (; st + U + WD <= steps; st += U) {
+    static_for<U>([&](auto I) { step(st, I, false); });
   }
   for (; st < steps; st += U) {
     static_for<U>([&](auto I) {
-      constexpr int i = I.value;
-      const int s = st + i;
-      if (s < steps) {
-        if (s + AD < steps) load_a(s + AD, av[i % AD]);
-        if (s + WD < steps) load_w(s + WD, wr[i % WD]);
-        compute(i & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s + 1 < steps) {
-          store_a((i + 1) & 1, av[(i + 1) % AD]);
-          store_w((i + 1) & 1, wr[(i + 1) % WD]);
-        }
-        __syncthreads();
-      }
+      if (st + I.value < steps) step(st, I, true);
     });
   }
 
@@ -428,9 +495,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs
   const int loc = a.bexp[tier][b];
   if ((unsigned)loc >= (unsigned)(tier ? a.E3 : a.E4)) return;
   __shared__ GemmSmem<BM> sm;
-  if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3>(a, tier, b, loc, tile, sm);
-  else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4>(a, tier, b, loc, tile, sm);
-  else gemm_tile<BM, W13, kPfMxfp4>(a, tier, b, loc, tile, sm);
+  if (a.vec_scales) {
+    if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3, true>(a, tier, b, loc, tile, sm);
+    else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4, true>(a, tier, b, loc, tile, sm);
+    else gemm_tile<BM, W13, kPfMxfp4, true>(a, tier, b, loc, tile, sm);
+  } else {
+    if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3, false>(a, tier, b, loc, tile, sm);
+    else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4, false>(a, tier, b, loc, tile, sm);
+    else gemm_tile<BM, W13, kPfMxfp4, false>(a, tier, b, loc, tile, sm);
+  }
 }
 
 // x16[t] = fp16(x[t] * 2^-e[t]), e[t] putting the token's largest |x| in [2^14, 2^15)
@@ -477,6 +550,13 @@ static GemmFn pick_gemm(int bm) {
     case 128: return grouped_gemm_kernel<128, W13>;
   }
   return nullptr;
+}
+
+// scale rows of whole, aligned 16-byte vectors of 8 K steps (512 K values), both tiers
+static int vec_scales_ok(const PrefillArgs& a) {
+  const bool rows = a.K % (8 * kBK) == 0;
+  const bool al = (reinterpret_cast<uintptr_t>(a.ks) % 16 == 0) && (reinterpret_cast<uintptr_t>(a.ns) % 16 == 0);
+  return rows && al ? 1 : 0;
 }
 
 // blocks of the 1-D GEMM grid: whole XCD groups of expert blocks times column tiles
@@ -535,6 +615,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     b.xe = xe;
     b.h_out = h;
     b.ntile = L.I / (kBN / 2);
+    b.vec_scales = vec_scales_ok(b);
     GemmFn fn = pick_gemm<true>(bm);
     if (!fn) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(gemm_grid(nblk, b.ntile)), dim3(kPfThreads), 0, s, b);
@@ -550,6 +631,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     c.o_out = o;
     c.topk_w = w;
     c.ntile = L.H / kBN;
+    c.vec_scales = vec_scales_ok(c);
     GemmFn fn = pick_gemm<false>(bm);
     if (!fn) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(gemm_grid(nblk, c.ntile)), dim3(kPfThreads), 0, s, c);
