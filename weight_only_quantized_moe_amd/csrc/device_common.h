@@ -147,7 +147,9 @@ __device__ __forceinline__ uint32_t nf3_pair_field(uint32_t d0, uint32_t d1, uin
 // ---------------------------------------------------------------------------
 // cross-lane exchange without the LDS crossbar
 // ---------------------------------------------------------------------------
-// xlane<B>(v) returns v from the partner lane of a butterfly step on lane bit B:
+// xlane<B>(v) returns v from the partner lane of a butterfly step on lane bit B
+// (every lane has a partner, so the DPP moves may zero-fill: that lets the compiler fold
+// them into the consuming add or max):
 // lane ^ 1, ^ 3, ^ 7, ^ 15 (DPP quad permute, row half-mirror, row mirror) for B <= 8,
 // lane ^ 16 and lane ^ 32 (v_permlane16_swap / v_permlane32_swap plus a select). Each
 // partner differs from the lane in bit B and only below it, so a sequence of steps over
@@ -156,13 +158,13 @@ template <int B>
 __device__ __forceinline__ uint32_t xlane_u32(uint32_t v) {
   static_assert(B == 1 || B == 2 || B == 4 || B == 8 || B == 16 || B == 32, "butterfly bit");
   if constexpr (B == 1) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true);   // quad [1,0,3,2]
   } else if constexpr (B == 2) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x1B, 0xF, 0xF, false);   // quad [3,2,1,0]
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x1B, 0xF, 0xF, true);   // quad [3,2,1,0]
   } else if constexpr (B == 4) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // row half-mirror
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true);  // row half-mirror
   } else if constexpr (B == 8) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // row mirror
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true);  // row mirror
   } else if constexpr (B == 16) {
     const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
     return (threadIdx.x & 16) ? r[0] : r[1];
@@ -213,6 +215,10 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// z * sigmoid(z) with the hardware reciprocal (1 ulp) in place of an IEEE division:
+// exp(-z) = inf for z < -88 gives rcp = 0 and -0, the limit
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 }  // namespace hmoe
