@@ -38,7 +38,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kPfThreads = 256;
 constexpr int kBK = 64;         // K per step (one NF3 group)
 constexpr int kBN = 128;        // weight rows per tile
-constexpr int kWeightAhead = 4; // steps between a weight load and its decode
 constexpr int kActAhead = 2;    // steps between an activation load and its LDS store
 constexpr int kPipeGroup = 8;   // unrolled steps (a multiple of both distances, 2 and 8)
 constexpr int kXcdGroup = 1;    // expert blocks per XCD assignment unit
@@ -125,12 +124,6 @@ struct GemmSmem {
   int sRef[kBN];          // MXFP4: largest E8M0 byte; NF3: largest fp16 scale exponent
 };
 
-// One K step of one thread's weight unit (32 elements of one tile row), raw.
-struct WRaw {
-  uint4 q;     // FP4: 16 code bytes; NF3: 12 code bytes in x, y, z
-  uint32_t s;  // NVFP4: two E4M3 bytes; MXFP4: one E8M0 byte; NF3: fp16 group scale
-};
-
 // NVFP4 16-element block (two code words) -> 8 fp16 pairs, exact (see the header).
 __device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32_t sbyte,
                                                 uint32_t* w) {
@@ -167,36 +160,70 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   const size_t hbase = (size_t)(tier ? a.hrow1 : 0) + (size_t)b * BM;
   const int steps = a.K / kBK;
 
-  // ---- this thread's weight unit of every step: tile row r, half uu (32 elements)
-  const int r = tid >> 1, uu = tid & 1;
-  const int wrow = W13 ? (r < kBN / 2 ? n0 + r : a.I + n0 + (r - kBN / 2)) : n0 + r;
+  // ---- weight units. Thread (wave w, lane l) owns tile rows rA = 32 w + (l >> 2) and
+  // rB = rA + 16 and, of every pair of steps, quarter p = l & 3 of each row's two-step
+  // code segment (a quarter is one step's half row: step 2k + (p >> 1), half p & 1).
+  // It loads quarter p of rA and quarter p ^ 2 of rB, so one load instruction reads 16
+  // whole 64-byte (NF3: 48-byte) segments instead of 32 half-used ones, and the thread
+  // ends up with one unit of each step: for step parity e the unit of row rowE[e], from
+  // the rA load when (p >> 1) == e. Both rows have the same XOR swizzle (rA = rB mod 8).
+  const int q4 = lane >> 2, p4 = lane & 3;
+  const int hp = p4 >> 1, uu = p4 & 1;
+  const int rA = 32 * wave + q4, rB = rA + 16;
+  const int rowE[2] = {hp == 0 ? rA : rB, hp == 1 ? rA : rB};
+  auto wrow_of = [&](int tr) {
+    return W13 ? (tr < kBN / 2 ? n0 + tr : a.I + n0 + (tr - kBN / 2)) : n0 + tr;
+  };
   const int RB = FMT == kPfNf3 ? 3 * a.K / 8 : a.K / 2;  // code bytes per row
   const int CB = FMT == kPfNf3 ? 24 : 32;                 // code bytes per row per step
-  const uint8_t* qrow = (FMT == kPfNf3 ? a.nq : a.kq) + ((size_t)loc * a.rows_w + wrow) * RB +
-                        (FMT == kPfNf3 ? 12 : 16) * uu;
-  const uint8_t* s8row = a.ks + ((size_t)loc * a.rows_w + wrow) * (a.K / (FMT == kPfNvfp4 ? 16 : 32));
-  const uint16_t* s16row = a.ns + ((size_t)loc * a.rows_w + wrow) * (a.K / 64);
-  // codes of step st; the scale word comes from load_s (one load per step) or from a
-  // vector of 8 steps' scales (VS)
-  auto load_q = [&](int st, WRaw& w) {
-    if constexpr (FMT == kPfNf3) {
-      const uint3 v = *reinterpret_cast<const uint3*>(qrow + st * CB);
-      w.q = make_uint4(v.x, v.y, v.z, 0u);
-    } else {
-      w.q = *reinterpret_cast<const uint4*>(qrow + st * CB);
-    }
+  const int HB = CB / 2;                                  // code bytes of a half row step
+  const uint8_t* qbase = FMT == kPfNf3 ? a.nq : a.kq;
+  const size_t row0 = (size_t)loc * a.rows_w;
+  const uint8_t* qA = qbase + (row0 + wrow_of(rA)) * RB + HB * p4;
+  const uint8_t* qB = qbase + (row0 + wrow_of(rB)) * RB + HB * (p4 ^ 2);
+  const int SRB = FMT == kPfNf3 ? a.K / 32 : a.K / (FMT == kPfNvfp4 ? 16 : 32);  // scale bytes per row
+  const uint8_t* sE[2] = {a.ks, a.ks};
+  if (FMT == kPfNf3) {
+    sE[0] = reinterpret_cast<const uint8_t*>(a.ns) + (row0 + wrow_of(rowE[0])) * SRB;
+    sE[1] = reinterpret_cast<const uint8_t*>(a.ns) + (row0 + wrow_of(rowE[1])) * SRB;
+  } else {
+    sE[0] = a.ks + (row0 + wrow_of(rowE[0])) * SRB;
+    sE[1] = a.ks + (row0 + wrow_of(rowE[1])) * SRB;
+  }
+  // raw units of one pair of steps: x from row rA, y from row rB (scale words only
+  // without VS; with VS they come from the per-parity scale vectors)
+  struct PairRaw {
+    uint4 qx, qy;
+    uint32_t sx, sy;
   };
-  auto load_s = [&](int st) -> uint32_t {
-    if constexpr (FMT == kPfNf3) return s16row[st];
-    else if constexpr (FMT == kPfNvfp4) return *reinterpret_cast<const uint16_t*>(s8row + 4 * st + 2 * uu);
-    else return s8row[2 * st + uu];
+  // scale word of row rowE[e], step st, this thread's half (one load)
+  auto load_s = [&](int e, int st) -> uint32_t {
+    if constexpr (FMT == kPfNf3) return reinterpret_cast<const uint16_t*>(sE[e])[st];
+    else if constexpr (FMT == kPfNvfp4) return *reinterpret_cast<const uint16_t*>(sE[e] + 4 * st + 2 * uu);
+    else return sE[e][2 * st + uu];
+  };
+  auto load_pair = [&](int k, PairRaw& w) {
+    if constexpr (FMT == kPfNf3) {
+      const uint3 x = *reinterpret_cast<const uint3*>(qA + 2 * k * CB);
+      const uint3 y = *reinterpret_cast<const uint3*>(qB + 2 * k * CB);
+      w.qx = make_uint4(x.x, x.y, x.z, 0u);
+      w.qy = make_uint4(y.x, y.y, y.z, 0u);
+    } else {
+      w.qx = *reinterpret_cast<const uint4*>(qA + 2 * k * CB);
+      w.qy = *reinterpret_cast<const uint4*>(qB + 2 * k * CB);
+    }
+    if constexpr (!VS) {
+      // the x unit is step 2k + hp of rA = rowE[hp]; the y unit the other step of rB
+      w.sx = load_s(hp, 2 * k + hp);
+      w.sy = load_s(hp ^ 1, 2 * k + (hp ^ 1));
+    }
   };
   constexpr int SG = 8;                         // steps per scale vector
   constexpr int SW = FMT == kPfNvfp4 ? 8 : 4;   // dwords per scale vector
   typedef uint32_t SVec[SW];
-  auto load_sv = [&](int grp, SVec& v) {
-    const uint4* p = FMT == kPfNf3 ? reinterpret_cast<const uint4*>(s16row + SG * grp)
-                                   : reinterpret_cast<const uint4*>(s8row + (FMT == kPfNvfp4 ? 4 : 2) * SG * grp);
+  // scale vector of row rowE[e], steps SG grp .. SG grp + SG - 1
+  auto load_sv = [&](int e, int grp, SVec& v) {
+    const uint4* p = reinterpret_cast<const uint4*>(sE[e] + (FMT == kPfNvfp4 ? 4 : 2) * SG * grp);
     const uint4 v0 = p[0];
     v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
     if constexpr (FMT == kPfNvfp4) {
@@ -213,40 +240,48 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   };
 
   // ---- per-row reference exponent (MXFP4: largest E8M0 byte; NF3: largest fp16
-  // exponent field of the row's group scales), the two threads of a row splitting it;
-  // the loads of a thread's share are independent, so they are issued together
-  int ref = 0;
-  if constexpr (FMT != kPfNvfp4 && VS) {
-    const uint4* p = FMT == kPfNf3 ? reinterpret_cast<const uint4*>(s16row)
-                                   : reinterpret_cast<const uint4*>(s8row);
-    const int nv = steps / SG;  // 16-byte vectors per row
-#pragma unroll 4
-    for (int c = uu; c < nv; c += 2) {
-      const uint4 v = p[c];
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  // exponent field of the row's group scales) of rows rowE[0] and rowE[1], the four
+  // lanes of a quad splitting each row's scales (lanes p and p ^ 2 hold the same two
+  // rows, swapped); the loads of a lane's share are independent and issued together
+  int refE[2] = {0, 0};
+  if constexpr (FMT != kPfNvfp4) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (FMT == kPfMxfp4) {
-          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 0, 8));
-          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 8, 8));
-          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 16, 8));
-          ref = max(ref, (int)(d[e] >> 24));
-        } else {
-          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 10, 5));
-          ref = max(ref, (int)__builtin_amdgcn_ubfe(d[e], 26, 5));
+    for (int e = 0; e < 2; ++e) {
+      int ref = 0;
+      if constexpr (VS) {
+        const uint4* pv = reinterpret_cast<const uint4*>(sE[e]);
+        const int nv = steps / SG;  // 16-byte vectors per row
+#pragma unroll 4
+        for (int c = uu; c < nv; c += 2) {
+          const uint4 v = pv[c];
+          const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (FMT == kPfMxfp4) {
+              ref = max(ref, (int)__builtin_amdgcn_ubfe(d[i], 0, 8));
+              ref = max(ref, (int)__builtin_amdgcn_ubfe(d[i], 8, 8));
+              ref = max(ref, (int)__builtin_amdgcn_ubfe(d[i], 16, 8));
+              ref = max(ref, (int)(d[i] >> 24));
+            } else {
+              ref = max(ref, (int)__builtin_amdgcn_ubfe(d[i], 10, 5));
+              ref = max(ref, (int)__builtin_amdgcn_ubfe(d[i], 26, 5));
+            }
+          }
         }
+      } else if constexpr (FMT == kPfMxfp4) {
+#pragma unroll 8
+        for (int i = uu; i < a.K / 32; i += 2) ref = max(ref, (int)sE[e][i]);
+      } else {
+        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(sE[e]);
+#pragma unroll 8
+        for (int i = uu; i < a.K / 64; i += 2) ref = max(ref, (int)((s16[i] >> 10) & 0x1F));
       }
+      refE[e] = max(ref, xlane_i<1>(ref));  // lanes p and p ^ 1 share row rowE[e]
     }
-  } else if constexpr (FMT == kPfMxfp4) {
-#pragma unroll 8
-    for (int i = uu; i < a.K / 32; i += 2) ref = max(ref, (int)s8row[i]);
-  } else if constexpr (FMT == kPfNf3) {
-#pragma unroll 8
-    for (int i = uu; i < a.K / 64; i += 2) ref = max(ref, (int)((s16row[i] >> 10) & 0x1F));
-  }
-  if (FMT != kPfNvfp4) {
-    ref = max(ref, __shfl_xor(ref, 1));
-    if (uu == 0) sm.sRef[r] = ref;
+    if (uu == 0) {
+      sm.sRef[rowE[0]] = refE[0];
+      sm.sRef[rowE[1]] = refE[1];
+    }
   }
   if (FMT == kPfNf3) {
     // thread t writes fields (t >> 5) + 8 i of column t & 31: low code t >> 5, high i
@@ -258,15 +293,18 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   }
   const uint32_t* lut = sm.lut + (lane & 31);
 
-  // decodes one raw unit into the B stage: 16 fp16 pairs, four 16-byte chunks
-  auto store_w = [&](int buf, const WRaw& w) {
+  // decodes the unit of step parity e (codes q, scale word sw) into the B stage: 16 fp16
+  // pairs, four 16-byte chunks of row rowE[e]
+  auto store_w = [&](int buf, int e, const uint4& q, uint32_t sw) {
+    const int r = rowE[e];
+    const int ref = refE[e];
     uint32_t v[16];
     if constexpr (FMT == kPfNvfp4) {
-      nvfp4_block_f16(w.q.x, w.q.y, w.s & 0xFFu, v);
-      nvfp4_block_f16(w.q.z, w.q.w, (w.s >> 8) & 0xFFu, v + 8);
+      nvfp4_block_f16(q.x, q.y, sw & 0xFFu, v);
+      nvfp4_block_f16(q.z, q.w, (sw >> 8) & 0xFFu, v + 8);
     } else if constexpr (FMT == kPfMxfp4) {
-      const float so = e8m0_scale_operand((uint32_t)max((int)w.s - ref + 127, 0));
-      const uint32_t qq[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+      const float so = e8m0_scale_operand((uint32_t)max((int)sw - ref + 127, 0));
+      const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[4 * i + 0] = e2m1x2_f16<0>(qq[i], so);
@@ -275,8 +313,8 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
         v[4 * i + 3] = e2m1x2_f16<3>(qq[i], so);
       }
     } else {
-      const uint32_t d0 = w.q.x, d1 = w.q.y, d2 = w.q.z;
-      const _Float16 mu = (_Float16)__builtin_ldexpf(fp16_to_f32(w.s), 15 - ref);
+      const uint32_t d0 = q.x, d1 = q.y, d2 = q.z;
+      const _Float16 mu = (_Float16)__builtin_ldexpf(fp16_to_f32(sw), 15 - ref);
       const f16x2 m = {mu, mu};
       v[0] = mul_f16x2(lut[nf3_pair_field<0>(d0, d1, d2) << 5], m);
       v[1] = mul_f16x2(lut[nf3_pair_field<1>(d0, d1, d2) << 5], m);
@@ -366,70 +404,82 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
     }
   };
 
-  // ---- pipeline. Raw weight units are loaded WD steps ahead into a ring of WD
-  // register slots and decoded into the free LDS stage one step ahead; activations
-  // are loaded AD steps ahead into AD register sets. Step s uses weight slot s % WD
-  // and activation set s % AD, so a group of U steps (a multiple of WD, AD and the
-  // two LDS stages) names every slot at compile time. Each step issues its loads in
-  // the order they are consumed (vector memory completes in order), and the stores
-  // of the next stage stay behind the MFMAs. Whole groups run unguarded; the last
-  // steps run guarded.
-  constexpr int WD = kWeightAhead, AD = kActAhead, U = kPipeGroup;
-  static_assert(U % WD == 0 && U % AD == 0 && U % 2 == 0 && U % SG == 0 && WD <= SG,
-                "pipeline group");
-  WRaw wr[WD];
+  // ---- pipeline. The raw units of step pair k are loaded at step 2k - 3 into pair
+  // slot k % 2 (a slot is free once its pair's second step has been decoded, at step
+  // 2k - 4) and decoded into the free LDS stage one step ahead; activations are loaded
+  // AD steps ahead into AD register sets. A group of U steps (a multiple of 2 pairs,
+  // AD, the two LDS stages and a scale vector) names every slot at compile time. Each
+  // step issues its loads in the order they are consumed (vector memory completes in
+  // order), and the stores of the next stage stay behind the MFMAs. Whole groups run
+  // unguarded; the last steps run guarded (steps is even: K is a multiple of 128).
+  constexpr int AD = kActAhead, U = kPipeGroup;
+  static_assert(U % 4 == 0 && U % AD == 0 && U % SG == 0, "pipeline group");
+  PairRaw pr[2];
   uint4 av[AD][S::A_PER];
-  SVec scur = {}, snext = {};  // VS: scale vectors of the current and the next group of SG steps
-  if constexpr (VS) load_sv(0, scur);
+  // VS: per-parity scale vectors of the current and the next group of SG steps
+  SVec scur[2] = {}, snext[2] = {};
+  if constexpr (VS) {
+    load_sv(0, 0, scur[0]);
+    load_sv(1, 0, scur[1]);
+  }
   static_for<AD>([&](auto i) {
     if (i.value < steps) load_a(i.value, av[i.value]);
   });
-  static_for<WD>([&](auto i) {
-    if (i.value < steps) {
-      load_q(i.value, wr[i.value]);
-      if constexpr (VS) wr[i.value].s = scale_of(scur, i);
-      else wr[i.value].s = load_s(i.value);
-    }
-  });
+  load_pair(0, pr[0]);
+  if (2 < steps) load_pair(1, pr[1]);
+  // unit of step t (parity E) from pair slot (t / 2) % 2; VC: the current scale
+  // vectors hold step t (else the next ones do)
+  auto unit_store = [&](int buf, auto E, auto TS, auto VC, const PairRaw& w) {
+    constexpr int e = decltype(E)::value;
+    const bool from_x = hp == e;
+    const uint4 q = from_x ? w.qx : w.qy;
+    uint32_t sw;
+    if constexpr (VS) sw = scale_of(VC.value ? scur[e] : snext[e], TS);
+    else sw = from_x ? w.sx : w.sy;
+    store_w(buf, e, q, sw);
+  };
   __syncthreads();  // table, reference exponents
   store_a(0, av[0]);
-  store_w(0, wr[0]);
+  unit_store(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+             std::true_type{}, pr[0]);
   __syncthreads();
   // step st = group base + i: MFMAs on stage i & 1; stage (i + 1) & 1 takes the
-  // activations and raw weights of step st + 1; loads fill the activation set of
-  // st + AD and the weight slot of st + WD (its scale from the current group's vector,
-  // or the next one's, requested at the group's first step)
+  // activations and the raw unit of step st + 1; loads fill the activation set of
+  // st + AD and, at odd steps, pair slot of pair (st + 3) / 2; a scale vector pair is
+  // requested at the group's first step for the next group
   auto step = [&](int st0, auto I, bool guarded) {
     constexpr int i = I.value;
     const int s = st0 + i;
     if constexpr (VS && i % SG == 0) {
-      if (!guarded || s + SG < steps) load_sv((s + SG) / SG, snext);
+      if (!guarded || s + SG < steps) {
+        load_sv(0, (s + SG) / SG, snext[0]);
+        load_sv(1, (s + SG) / SG, snext[1]);
+      }
     }
     if (!guarded || s + AD < steps) load_a(s + AD, av[(i + AD) % AD]);
-    if (!guarded || s + WD < steps) {
-      load_q(s + WD, wr[i % WD]);
-      if constexpr (VS) {
-        constexpr int t = (i + WD) % SG;
-        if constexpr ((i % SG) + WD < SG) wr[i % WD].s = scale_of(scur, std::integral_constant<int, t>{});
-        else wr[i % WD].s = scale_of(snext, std::integral_constant<int, t>{});
-      } else {
-        wr[i % WD].s = load_s(s + WD);
-      }
+    if constexpr (i % 2 == 1) {
+      if (!guarded || s + 3 < steps) load_pair((s + 3) / 2, pr[((i + 3) / 2) % 2]);
     }
     compute(i & 1);
     __builtin_amdgcn_sched_barrier(0);
     if (!guarded || s + 1 < steps) {
       store_a((i + 1) & 1, av[(i + 1) % AD]);
-      store_w((i + 1) & 1, wr[(i + 1) % WD]);
+      constexpr int t = i + 1;  // step decoded now, relative to the group base
+      unit_store((i + 1) & 1, std::integral_constant<int, t & 1>{},
+                 std::integral_constant<int, t % SG>{},
+                 std::integral_constant<bool, (t < SG)>{}, pr[(t / 2) % 2]);
     }
     __syncthreads();
     if constexpr (VS && i % SG == SG - 1) {
 #pragma unroll
-      for (int e = 0; e < SW; ++e) scur[e] = snext[e];
+      for (int e = 0; e < SW; ++e) {
+        scur[0][e] = snext[0][e];
+        scur[1][e] = snext[1][e];
+      }
     }
   };
   int st = 0;
-  for (; st + U + WD <= steps; st += U) {
+  for (; st + U + 3 <= steps; st += U) {
     static_for<U>([&](auto I) { step(st, I, false); });
   }
   for (; st < steps; st += U) {
