@@ -112,9 +112,8 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
         log(f"{w.name}: generated packed layer in {time.time() - t0:.1f}s")
     bm = packed["bit_map"]
     fmt = hm.KEPT_NVFP4 if packed["kept_format"] == "nvfp4" else hm.KEPT_MXFP4
-    if block_m is None:
-        block_m = 128 if w.M > hm.DECODE_MAX_M else 32
-    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, block_m)
+    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, block_m or 0)
+    block_m = hm.moe_layer_query(layer)["block_m"]
     base = hm.DeviceWeights(packed)
     layer_bytes = base.nbytes()
     if copies is None:
@@ -258,7 +257,8 @@ def main():
                     help="only copy MIB mebibytes device to device five times (the plain copy "
                          "the HBM traffic counters are scaled by) and exit")
     ap.add_argument("--block-m", type=int, default=None,
-                    help="prefill GEMM rows per expert block (16/32/64/128; default 128)")
+                    help="prefill GEMM rows per expert block (16/32/64/128; default: the library picks "
+                         "from max_tokens * top_k / E)")
     args = ap.parse_args()
 
     if args.gpus != 1:

@@ -80,8 +80,9 @@ enum { HMOE_STAGE_ROUTE = 0, HMOE_STAGE_W13 = 1, HMOE_STAGE_W2 = 2, HMOE_STAGE_C
  *                runs uniform NVFP4 whatever this says ([P1])
  *   bit_map      host array of E bytes, each 4 (kept) or 3 (NF3); copied; NULL means
  *                every expert is in the kept tier, as NVFP4
- *   block_m      prefill rows per expert block for moe_align: 16, 32, 64 or 128; 0 picks
- *                the library default (32) */
+ *   block_m      prefill rows per expert block for moe_align: 16, 32, 64 or 128; 0 lets
+ *                the library pick from t = max_tokens * top_k / E: 16 below t = 4, 32
+ *                below 24, 64 below 64, else 128 */
 typedef struct hmoe_layer_desc {
     int32_t num_experts;
     int32_t hidden;

@@ -74,7 +74,15 @@ def test_query_and_tiers():
     assert q["cap_kept"] == -(-(64 * 2 + 3 * 15) // 16) * 16 and q["cap_nf3"] == -(-(128 + 5 * 15) // 16) * 16
     # no bit map: uniform NVFP4 whatever the kept format says
     q2 = hm.moe_layer_query(hm.moe_layer_create(8, 256, 128, 2, 4, hm.KEPT_MXFP4, None))
-    assert q2["kept_format"] == hm.KEPT_NVFP4 and q2["num_nf3"] == 0 and q2["block_m"] == 32
+    assert q2["kept_format"] == hm.KEPT_NVFP4 and q2["num_nf3"] == 0 and q2["block_m"] == 16
+
+
+@pytest.mark.parametrize("max_tokens,expect", [(1, 16), (127, 16), (128, 32), (767, 32), (768, 64),
+                                               (2047, 64), (2048, 128), (4096, 128)])
+def test_default_block_m(max_tokens, expect):
+    # block_m 0: chosen from t = max_tokens * k / E (here E = 256, k = 8: t = max_tokens / 32)
+    layer = hm.moe_layer_create(256, 256, 128, 8, max_tokens, hm.KEPT_NVFP4, None, 0)
+    assert hm.moe_layer_query(layer)["block_m"] == expect
 
 
 def test_scratch_planner_covers_every_region():
