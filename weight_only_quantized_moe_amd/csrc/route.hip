@@ -11,62 +11,105 @@ namespace hmoe {
 
 constexpr int kRouteWaves = 4;  // tokens per block of the general route kernel
 
-// One argmax butterfly step on (value, id): keep the larger value, ties to the lower
-// id (a total order, so every lane of the wave ends with the same winner).
-template <int B>
-__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
-  const float ov = xlane<B>(bv);
-  const int oi = xlane_i<B>(bi);
-  if (ov > bv || (ov == bv && oi < bi)) {
-    bv = ov;
-    bi = oi;
-  }
+// Per-wave LDS of the top-k: the k selected (key, id, logit) in id order, then in rank
+// order.
+struct TopkLds {
+  __attribute__((aligned(16))) uint32_t key[kMaxTopK];
+  __attribute__((aligned(16))) int32_t id[kMaxTopK];
+  float v[kMaxTopK];
+  int32_t rid[kMaxTopK];
+  float rv[kMaxTopK];
+};
+
+// order-preserving unsigned image of a float (NaN excluded): larger float, larger key
+__device__ __forceinline__ uint32_t order_key(float t) {
+  const uint32_t b = __float_as_uint(t);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
 // Top-k of one token's logits row by one wave; each lane holds NV >= E / 64 logits
-// (lane + 64 i). Experts rank by logit, descending, ties to the lower id; each of the
-// k rounds takes every lane's best remaining logit and a butterfly argmax over the
-// wave. Lane j < k ends with the j-th selection in (sel_v, sel_id). Weights: softmax
-// over the selected logits, in fp64, rounded once to fp32.
+// (expert lane + 64 i). Experts rank by logit, descending, ties to the lower id; NaN
+// counts as -inf and -0 as +0. The k-th largest logit comes from a bitwise search over
+// its order-preserving 32-bit key (one ballot count per bit); the keys above it and,
+// by ascending id, as many of those equal to it as needed make the selection, which is
+// ranked by pairwise comparison in LDS. Lane j < k ends with the j-th selection in
+// (sel_v, sel_id). Weights: softmax over the selected logits, in fp64, rounded once to
+// fp32.
 template <int NV>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
                                             int32_t* __restrict__ ids_out,
-                                            float* __restrict__ w_out, int32_t* lds_ids) {
+                                            float* __restrict__ w_out, int32_t* lds_ids,
+                                            TopkLds& tl) {
   float v[NV];
+  uint32_t u[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + kWave * i;
-    const float t = (e < E) ? row[e] : -INFINITY;
-    v[i] = (t != t) ? -INFINITY : t;  // NaN ranks below every number: a total order
+    float t = (e < E) ? row[e] : -INFINITY;
+    t = (t != t) ? -INFINITY : t;  // NaN ranks with -inf: a total order
+    t = (t == 0.0f) ? 0.0f : t;    // -0 ties with +0
+    v[i] = t;
+    u[i] = (e < E) ? order_key(t) : 0u;  // -inf has key 0x007FFFFF: padding ranks last
   }
-  uint32_t taken = 0;
-  float sel_v = 0.0f;
-  int sel_id = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // tau = the largest key with at least k keys >= tau (the k-th largest key), two bits
+  // per step: the counts at the three candidate digits are independent
+  uint32_t tau = 0;
+#pragma unroll
+  for (int bit = 30; bit >= 0; bit -= 2) {
+    int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int e = lane + kWave * i;
-      const bool ok = (e < E) && !((taken >> i) & 1u);
-      // ids grow with i inside a lane, so a strict > keeps the lowest id on ties
-      if (ok && (v[i] > bv || bi == 0x7FFFFFFF)) {
-        bv = v[i];
-        bi = e;
-      }
+      n1 += __popcll(__ballot(u[i] >= (tau | (1u << bit))));
+      n2 += __popcll(__ballot(u[i] >= (tau | (2u << bit))));
+      n3 += __popcll(__ballot(u[i] >= (tau | (3u << bit))));
     }
-    argmax_step<32>(bv, bi);
-    argmax_step<16>(bv, bi);
-    argmax_step<8>(bv, bi);
-    argmax_step<4>(bv, bi);
-    argmax_step<2>(bv, bi);
-    argmax_step<1>(bv, bi);
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-    if (lane == j) {
-      sel_v = bv;
-      sel_id = bi;
-    }
+    tau |= (uint32_t)((n1 >= k) + (n2 >= k) + (n3 >= k)) << bit;
   }
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) above += __popcll(__ballot(u[i] > tau));
+  const int need = k - above;  // ties taken, lowest ids first
+  int ties_before = 0, placed = 0;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const uint64_t tie = __ballot(u[i] == tau);
+    const bool sel = u[i] > tau || (u[i] == tau && ties_before + __popcll(tie & lt) < need);
+    const uint64_t sb = __ballot(sel);
+    if (sel) {
+      const int pos = placed + __popcll(sb & lt);
+      tl.key[pos] = u[i];
+      tl.id[pos] = lane + kWave * i;
+      tl.v[pos] = v[i];
+    }
+    placed += __popcll(sb);
+    ties_before += __popcll(tie);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < k) {
+    const uint32_t uj = tl.key[lane];
+    const int ej = tl.id[lane];
+    const float vj = tl.v[lane];
+    // the whole list at once (same address in every lane: broadcast reads)
+    uint32_t km[kMaxTopK];
+    int32_t im[kMaxTopK];
+#pragma unroll
+    for (int q = 0; q < kMaxTopK / 4; ++q) {
+      const uint4 kk = reinterpret_cast<const uint4*>(tl.key)[q];
+      const int4 ii = reinterpret_cast<const int4*>(tl.id)[q];
+      km[4 * q] = kk.x; km[4 * q + 1] = kk.y; km[4 * q + 2] = kk.z; km[4 * q + 3] = kk.w;
+      im[4 * q] = ii.x; im[4 * q + 1] = ii.y; im[4 * q + 2] = ii.z; im[4 * q + 3] = ii.w;
+    }
+    int rank = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxTopK; ++m)
+      rank += (m < k && (km[m] > uj || (km[m] == uj && im[m] < ej))) ? 1 : 0;
+    tl.rid[rank] = ej;
+    tl.rv[rank] = vj;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const float sel_v = lane < k ? tl.rv[lane] : 0.0f;
+  const int sel_id = lane < k ? tl.rid[lane] : 0;
   const float v0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(sel_v), 0));
   const double ex = (lane < k) ? exp((double)sel_v - (double)v0) : 0.0;
   double sum = ex;
@@ -86,12 +129,13 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
 // route_token with NV = the smallest power of two covering E / 64 logits per lane
 __device__ __forceinline__ void route_token_any(const float* __restrict__ row, int E, int k,
                                                 int lane, int32_t* __restrict__ ids_out,
-                                                float* __restrict__ w_out, int32_t* lds_ids) {
-  if (E <= 64) route_token<1>(row, E, k, lane, ids_out, w_out, lds_ids);
-  else if (E <= 128) route_token<2>(row, E, k, lane, ids_out, w_out, lds_ids);
-  else if (E <= 256) route_token<4>(row, E, k, lane, ids_out, w_out, lds_ids);
-  else if (E <= 512) route_token<8>(row, E, k, lane, ids_out, w_out, lds_ids);
-  else route_token<16>(row, E, k, lane, ids_out, w_out, lds_ids);
+                                                float* __restrict__ w_out, int32_t* lds_ids,
+                                                TopkLds& tl) {
+  if (E <= 64) route_token<1>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
+  else if (E <= 128) route_token<2>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
+  else if (E <= 256) route_token<4>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
+  else if (E <= 512) route_token<8>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
+  else route_token<16>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each
@@ -109,11 +153,12 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const float* __restrict__ logits, int M, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ w) {
+  __shared__ TopkLds tl[kRouteWaves];
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
   if (t >= M) return;
   route_token_any(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k,
-                  nullptr);
+                  nullptr, tl[threadIdx.x >> 6]);
 }
 
 // Number of NF3-tier experts with id below 64 * chunk (the mask holds one bit per
@@ -143,6 +188,7 @@ constexpr int kGroupWaves = kDecodeMaxM;
 
 __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupArgs a, TierMask tm) {
   __shared__ int32_t s_ids[kDecodeMaxM * kMaxTopK];
+  __shared__ TopkLds s_topk[kGroupWaves];
   __shared__ uint32_t s_mask[kMaxExperts][4];   // slot bit masks (M * k <= 128 slots)
   __shared__ int32_t s_order[kMaxExperts];      // (tier, local) position -> expert or -1
   __shared__ int32_t s_pos[kMaxExperts];        // expert -> (tier, local) position
@@ -154,7 +200,7 @@ __global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupAr
   const uint64_t lt = (1ull << lane) - 1ull;
   if (wave < a.M)
     route_token_any(a.logits + (size_t)wave * a.E, a.E, a.k, lane, a.ids + wave * a.k,
-                a.w + wave * a.k, s_ids + wave * a.k);
+                    a.w + wave * a.k, s_ids + wave * a.k, s_topk[wave]);
   // tier map: one wave per 64-expert chunk, ranks by ballot
   for (int chunk = wave; chunk * kWave < a.E; chunk += kGroupWaves) {
     const int e = chunk * kWave + lane;
