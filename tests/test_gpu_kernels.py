@@ -91,6 +91,7 @@ def test_dequant_bit_exact(hm, case):
 @pytest.mark.parametrize("M,E,k,kind", [
     (1, 8, 2, "normal"), (7, 128, 8, "normal"), (64, 256, 8, "normal"), (1000, 1000, 16, "normal"),
     (300, 256, 8, "ties"), (33, 64, 64 // 4, "ties"), (5, 3, 3, "normal"), (20, 256, 1, "zeros"),
+    (40, 128, 8, "specials"), (9, 64, 16, "specials"),
 ])
 def test_route_matches_oracle(hm, M, E, k, kind):
     torch = torch_mod()
@@ -100,16 +101,30 @@ def test_route_matches_oracle(hm, M, E, k, kind):
     elif kind == "ties":
         lg = r.integers(-2, 3, (M, E)).astype(np.float32)
         lg[:, ::3] *= -1.0   # introduces -0.0 next to +0.0
-    else:
+    elif kind == "zeros":
         lg = np.zeros((M, E), np.float32)
         lg[:, 1::2] = -0.0
+    else:
+        # NaN (ranks below every number), -inf, and +-0, with the selection reaching down
+        # into the -inf and zero logits but not the NaNs
+        lg = r.standard_normal((M, E)).astype(np.float32)
+        lg[:, : E // 2] = -np.abs(lg[:, : E // 2]) - 1.0
+        lg[:, E // 2:] = np.nan
+        ninf = np.arange(E // 2) % 4 != 0 if k > 8 else np.arange(E // 2) % 7 == 1
+        lg[:, : E // 2][:, ninf] = -np.inf
+        lg[:, 2 : E // 2 : 9] = 0.0
+        lg[:, 4 : E // 2 : 9] = -0.0
+        lg[:, E - 1] = 0.5
     ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
     w = torch.empty((M, k), dtype=torch.float32, device="cuda")
     hm.moe_route(to_dev(lg), k, ids, w)
     torch.cuda.synchronize()
     ref_ids, ref_w = OL.route(lg, k)
     assert np.array_equal(ids.cpu().numpy(), ref_ids)
-    rel = np.abs(w.cpu().numpy().astype(np.float64) - ref_w) / ref_w
+    got = w.cpu().numpy().astype(np.float64)
+    nz = ref_w > 0          # -inf logits weigh exactly 0
+    assert np.all(got[~nz] == 0.0)
+    rel = np.abs(got[nz] - ref_w[nz]) / ref_w[nz]
     assert rel.max() <= 1e-6, rel.max()
 
 

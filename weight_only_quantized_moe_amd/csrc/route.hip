@@ -29,7 +29,7 @@ __device__ __forceinline__ uint32_t order_key(float t) {
 
 // Top-k of one token's logits row by one wave; each lane holds NV >= E / 64 logits
 // (expert lane + 64 i). Experts rank by logit, descending, ties to the lower id; NaN
-// counts as -inf and -0 as +0. The k-th largest logit comes from a bitwise search over
+// ranks below -inf and -0 ties with +0. The k-th largest logit comes from a bitwise search over
 // its order-preserving 32-bit key (one ballot count per bit); the keys above it and,
 // by ascending id, as many of those equal to it as needed make the selection, which is
 // ranked by pairwise comparison in LDS. Lane j < k ends with the j-th selection in
@@ -46,10 +46,12 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   for (int i = 0; i < NV; ++i) {
     const int e = lane + kWave * i;
     float t = (e < E) ? row[e] : -INFINITY;
-    t = (t != t) ? -INFINITY : t;  // NaN ranks with -inf: a total order
+    const bool nan = t != t;
+    t = nan ? -INFINITY : t;       // a NaN logit weighs as -inf in the softmax
     t = (t == 0.0f) ? 0.0f : t;    // -0 ties with +0
     v[i] = t;
-    u[i] = (e < E) ? order_key(t) : 0u;  // -inf has key 0x007FFFFF: padding ranks last
+    // keys: -inf is 0x007FFFFF, NaN 1 (below every number), padding 0 (last)
+    u[i] = (e < E) ? (nan ? 1u : order_key(t)) : 0u;
   }
   const uint64_t lt = (1ull << lane) - 1ull;
   // tau = the largest key with at least k keys >= tau (the k-th largest key), two bits
