@@ -576,17 +576,22 @@ __global__ __launch_bounds__(256) void prefill_x16_kernel(const uint16_t* __rest
   if (threadIdx.x == 0) xe[t] = e;
 }
 
-// y[t, n] = sum_j o[t*k + j, n] in fixed j order (the routing weight is already in o)
+// y[t, n..n+3] = sum_j o[t*k + j, n..n+3] in fixed j order (the routing weight is
+// already in o); four columns per thread, 16-byte loads (H is a multiple of 128)
 __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __restrict__ o, int M,
                                                               int k, int H,
                                                               uint16_t* __restrict__ y) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)M * H) return;
-  const size_t t = idx / H;
-  const size_t n = idx - t * H;
-  float acc = 0.0f;
-  for (int j = 0; j < k; ++j) acc += o[(t * k + j) * H + n];
-  y[idx] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // index of a 4-column group
+  const size_t nq = (size_t)M * (H / 4);
+  if (q >= nq) return;
+  const size_t t = q / (H / 4);
+  const size_t n = (q - t * (H / 4)) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float4 v = *reinterpret_cast<const float4*>(o + (t * k + j) * H + n);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  *reinterpret_cast<uint2*>(y + t * H + n) = make_uint2(pack_bf16(acc.x, acc.y), pack_bf16(acc.z, acc.w));
 }
 
 typedef void (*GemmFn)(PrefillArgs);
@@ -688,7 +693,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_COMBINE) {
-    const size_t n = (size_t)M * L.H;
+    const size_t n = (size_t)M * (L.H / 4);
     hipLaunchKernelGGL(prefill_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        o, M, L.k, L.H, y);
     return hipGetLastError();
