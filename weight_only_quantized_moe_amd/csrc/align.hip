@@ -62,10 +62,11 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
   __syncthreads();
   // padded exclusive offsets, one wave per tier, experts in ascending id
   if (wave < 2) {
-    int running = 0;
+    int running = 0, n_in_tier = 0;
     for (int base = 0; base < a.E; base += kWave) {
       const int e = base + lane;
       const bool in = e < a.E && (s_tc[e] >> 16) == wave;
+      n_in_tier += __popcll(__ballot(in));
       const int padded = in ? (s_cnt[e] + a.bm - 1) / a.bm * a.bm : 0;
       int incl = padded;
 #pragma unroll
@@ -82,8 +83,6 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
     }
     if (lane == 0) {
       // E_tier entries precede the terminal offset
-      int n_in_tier = 0;
-      for (int e = 0; e < a.E; ++e) n_in_tier += ((s_tc[e] >> 16) == wave);
       a.eoff[wave][n_in_tier] = running;
       a.npad[wave][0] = running;
     }

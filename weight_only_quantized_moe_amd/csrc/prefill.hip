@@ -556,23 +556,38 @@ __global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs
   }
 }
 
-// x16[t] = fp16(x[t] * 2^-e[t]), e[t] putting the token's largest |x| in [2^14, 2^15)
+// x16[t] = fp16(x[t] * 2^-e[t]), e[t] putting the token's largest |x| in [2^14, 2^15);
+// eight elements per thread and step (16-byte loads and stores; H is a multiple of 128)
 __global__ __launch_bounds__(256) void prefill_x16_kernel(const uint16_t* __restrict__ x, int H,
                                                           uint16_t* __restrict__ x16,
                                                           int32_t* __restrict__ xe) {
   __shared__ float red[4];
   const int t = blockIdx.x;
-  const uint16_t* row = x + (size_t)t * H;
+  const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  uint4* out = reinterpret_cast<uint4*>(x16 + (size_t)t * H);
+  const int n8 = H / 8;
   float mx = 0.0f;
-  for (int i = threadIdx.x; i < H; i += 256) mx = fmaxf(mx, fabsf(__uint_as_float((uint32_t)row[i] << 16)));
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const uint4 v = row[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[c])), fabsf(bf16_hi(w[c]))));
+  }
   mx = group_max<kWave>(mx);
   if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int ef = (int)((__float_as_uint(mx) >> 23) & 0xFF);
   const int e = mx > 0.0f ? (ef == 0 ? -126 : ef - 127) - 14 : 0;
-  for (int i = threadIdx.x; i < H; i += 256)
-    x16[(size_t)t * H + i] = (uint16_t)(pack_f16(__builtin_ldexpf(__uint_as_float((uint32_t)row[i] << 16), -e), 0.0f) & 0xFFFFu);
+  for (int i = threadIdx.x; i < n8; i += 256) {
+    const uint4 v = row[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      o[c] = pack_f16(__builtin_ldexpf(bf16_lo(w[c]), -e), __builtin_ldexpf(bf16_hi(w[c]), -e));
+    out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
   if (threadIdx.x == 0) xe[t] = e;
 }
 
