@@ -158,10 +158,10 @@ typedef struct hmoe_align_view {
  *   num_slots   int32 [max_distinct]: number of slots routed to each
  *   slots       int32 [max_distinct, 8]: those slots, ascending
  *   expert_tier int32 [E]: (tier << 16) | tier-local id of every expert
- *   passes      int32 [M * k, 4]: one record per slot, (slot, (tier << 16) | tier-local
- *               id, token, expert), grouped by expert in the order of `experts`,
- *               ascending slot within an expert; the decode GEMVs split their work
- *               over these records */
+ *   passes      int32 [M * k, 4]: one record per slot, in slot order: (slot,
+ *               (tier << 16) | tier-local id, token, expert); the decode GEMVs split
+ *               their work over these records (written by the ROUTE stage; the other
+ *               fields by the COMBINE stage, off the critical path) */
 typedef struct hmoe_decode_view {
     int32_t* counts;
     int32_t* experts;
@@ -229,8 +229,8 @@ hmoe_status moe_topk_view(const hmoe_layer* layer, void* scratch, int32_t** topk
 /* The layer forward ([P1] "How it works", [P2] "Summary"): y = sum over each token's
  * top-k experts of w[t, j] * SwiGLU_expert(x[t]), both tiers sharing one routing result
  * and one sum. x: bf16 bits [M, H]; router_logits: fp32 [M, E]; y: bf16 bits [M, H],
- * fully overwritten. M <= 8 takes the decode path (route + grouping, W13 + SwiGLU, W2 +
- * weighted combine); M > 8 the prefill path (route, per-tier align, grouped GEMM W13 +
+ * fully overwritten. M <= 8 takes the decode path (route + pass records, W13 + SwiGLU,
+ * W2 + weighted combine); M > 8 the prefill path (route, per-tier align, grouped GEMM W13 +
  * SwiGLU, grouped GEMM W2 + weighted combine). M = 0 is a no-op returning HMOE_OK.
  * Never allocates, synchronises or reads back: capturable in a HIP graph at fixed M.
  * Errors: HMOE_ERR_INVALID_ARG (null layer/weights, M < 0, a needed weight array NULL),
@@ -242,10 +242,11 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
 
 /* One stage of hybrid_moe_forward, for profiling: with the same arguments, calling
  * HMOE_STAGE_ROUTE, _W13, _W2 and _COMBINE in that order on one stream is exactly
- * hybrid_moe_forward. ROUTE is routing plus the decode grouping (M <= 8) or routing,
- * the per-tier align and the tokens' conversion to scaled fp16 (M > 8); W13 is the expert up projection with the fused
- * SwiGLU; W2 the down projection with the routing weight; COMBINE the fixed-order
- * top-k sum into y. Each stage reads what the previous stages left in scratch, so a
+ * hybrid_moe_forward. ROUTE is routing plus the per-slot pass records (M <= 8) or
+ * routing, the per-tier align and the tokens' conversion to scaled fp16 (M > 8); W13 is
+ * the expert up projection with the fused SwiGLU; W2 the down projection with the
+ * routing weight; COMBINE the fixed-order top-k sum into y (plus, for M <= 8, the
+ * decode grouping of moe_decode_view). Each stage reads what the previous stages left in scratch, so a
  * stage run out of order computes from stale scratch contents (no fault, since every
  * index it reads is bounds-checked or produced by ROUTE for this layer).
  * Errors: as hybrid_moe_forward, plus HMOE_ERR_INVALID_ARG for an unknown stage. */

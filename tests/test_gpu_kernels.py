@@ -155,9 +155,11 @@ def test_decode_grouping_bit_exact(hm, M):
     assert np.array_equal(et >> 16, tier) and np.array_equal(et & 0xFFFF, local)
     tids, tw = hm.moe_topk_view(layer, scratch, M)
     assert np.array_equal(tids.cpu().numpy(), ids)
-    # pass records: every slot once, grouped by expert in group order, slots ascending
+    # pass records: one per slot, in slot order: slot, tier code of its expert, token,
+    # expert
     passes = v["passes"].cpu().numpy()[: M * w.top_k]
-    want = [(s, (t << 16) | l, s // w.top_k, e) for (e, t, l, sl) in groups for s in sl]
+    want = [(s, (int(tier[e]) << 16) | int(local[e]), s // w.top_k, int(e))
+            for s, e in enumerate(ids.reshape(-1))]
     assert [tuple(int(c) for c in r) for r in passes] == want
 
 

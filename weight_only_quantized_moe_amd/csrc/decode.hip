@@ -608,11 +608,109 @@ __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
   }
 }
 
-// y[t, n] = sum_j w[t, j] * o[t*k + j, n], in fixed j order, rounded to bf16.
+// Decode grouping (M <= 8), kept for inspection (moe_decode_view): the distinct experts
+// the M * k slots touch, in tier order (kept tier by local index, then NF3), each with
+// its slots in ascending order, and the two counts.
+struct GroupSmem {
+  int32_t ids[kDecodeMaxM * kMaxTopK];
+  uint32_t mask[kMaxExperts][4];  // slot bit masks (M * k <= 128 slots)
+  int32_t order[kMaxExperts];     // (tier, local) position -> expert or -1
+  int32_t pos[kMaxExperts];       // expert -> (tier, local) position
+  int32_t d[kMaxExperts];         // expert -> group index
+};
+
+struct GroupArgs {
+  const int32_t* ids;  // [M * k] top-k ids
+  int M, E, k, E4;
+  int32_t* counts;     // [2]: distinct experts, distinct kept-tier experts
+  int32_t* experts;    // [max_distinct]
+  int32_t* nslots;     // [max_distinct]
+  int32_t* slots;      // [max_distinct, 8]
+};
+
+// built by one block of 256 threads
+__device__ __forceinline__ void decode_grouping(const GroupArgs& a, const TierMask& tm,
+                                                GroupSmem& sm) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int nslot = a.M * a.k;
+  for (int s = threadIdx.x; s < nslot; s += blockDim.x) sm.ids[s] = a.ids[s];
+  // tier positions: one wave per 64-expert chunk, ranks by ballot
+  for (int chunk = wave; chunk * kWave < a.E; chunk += nwaves) {
+    const int e = chunk * kWave + lane;
+    const bool in = e < a.E;
+    const bool nf3 = in && ((tm.w[e >> 5] >> (e & 31)) & 1u);
+    const uint64_t b = __ballot(nf3);
+    int below = 0;
+    for (int i = 0; i < 2 * chunk; ++i) below += __popc(tm.w[i]);
+    below += __popcll(b & lt);
+    if (in) {
+      sm.pos[e] = nf3 ? a.E4 + below : e - below;
+      sm.mask[e][0] = sm.mask[e][1] = sm.mask[e][2] = sm.mask[e][3] = 0u;
+    }
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < nslot; s += blockDim.x) {
+    const int e = sm.ids[s];
+    if ((unsigned)e < (unsigned)a.E) atomicOr(&sm.mask[e][s >> 5], 1u << (s & 31));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+    const bool touched = (sm.mask[e][0] | sm.mask[e][1] | sm.mask[e][2] | sm.mask[e][3]) != 0u;
+    sm.order[sm.pos[e]] = touched ? e : -1;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int running = 0, kept_distinct = 0;
+    for (int base = 0; base < a.E; base += kWave) {
+      const int p = base + lane;
+      const int e = (p < a.E) ? sm.order[p] : -1;
+      const bool f = e >= 0;
+      const uint64_t b = __ballot(f);
+      if (f) {
+        const int d = running + __popcll(b & lt);
+        const int n = __popc(sm.mask[e][0]) + __popc(sm.mask[e][1]) + __popc(sm.mask[e][2]) +
+                      __popc(sm.mask[e][3]);
+        sm.d[e] = d;
+        a.experts[d] = e;
+        a.nslots[d] = n < kDecodeMaxM ? n : kDecodeMaxM;
+      }
+      const int cnt = __popcll(b);
+      if (base + kWave <= a.E4) kept_distinct += cnt;
+      else if (base < a.E4) kept_distinct += __popcll(b & ((1ull << (a.E4 - base)) - 1ull));
+      running += cnt;
+    }
+    if (lane == 0) {
+      a.counts[0] = running;
+      a.counts[1] = kept_distinct;
+    }
+  }
+  __syncthreads();
+  // each slot at its rank among its expert's slots
+  for (int s = threadIdx.x; s < nslot; s += blockDim.x) {
+    const int e = sm.ids[s];
+    if ((unsigned)e >= (unsigned)a.E) continue;
+    int rank = 0;
+    for (int wd = 0; wd < (s >> 5); ++wd) rank += __popc(sm.mask[e][wd]);
+    rank += __popc(sm.mask[e][s >> 5] & ((1u << (s & 31)) - 1u));
+    if (rank < kDecodeMaxM) a.slots[sm.d[e] * kDecodeMaxM + rank] = s;
+  }
+}
+
+// y[t, n] = sum_j w[t, j] * o[t*k + j, n], in fixed j order, rounded to bf16. The last
+// block builds the decode grouping instead.
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ o,
                                                              const float* __restrict__ w, int M,
                                                              int k, int H,
-                                                             uint16_t* __restrict__ y) {
+                                                             uint16_t* __restrict__ y,
+                                                             GroupArgs ga, TierMask tm) {
+  if (blockIdx.x == gridDim.x - 1) {
+    __shared__ GroupSmem sm;
+    decode_grouping(ga, tm, sm);
+    return;
+  }
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= M * H) return;
   const int t = idx / H;
@@ -757,8 +855,20 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
   }
   if (stage == HMOE_STAGE_COMBINE) {
     const int n = M * L.H;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, o,
-                       reinterpret_cast<const float*>(base + P.topk_w), M, L.k, L.H, y);
+    GroupArgs ga;
+    ga.ids = reinterpret_cast<const int32_t*>(base + P.topk_ids);
+    ga.M = M;
+    ga.E = L.E;
+    ga.k = L.k;
+    ga.E4 = L.E4;
+    ga.counts = reinterpret_cast<int32_t*>(base + P.d_counts);
+    ga.experts = reinterpret_cast<int32_t*>(base + P.d_experts);
+    ga.nslots = reinterpret_cast<int32_t*>(base + P.d_nslots);
+    ga.slots = reinterpret_cast<int32_t*>(base + P.d_slots);
+    // one more block than the sum needs: it builds the grouping
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((n + 255) / 256 + 1), dim3(256), 0, s, o,
+                       reinterpret_cast<const float*>(base + P.topk_w), M, L.k, L.H, y, ga,
+                       make_tier_mask(L));
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -16,16 +16,14 @@ namespace hmoe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kDecodeMaxM = HMOE_DECODE_MAX_M;
-// decode group record (int32 words): expert id, tier code, slot count, 0, slots[8], 0 x 4
-constexpr int kGroupRec = 16;
-// decode pass record (int4), one per (token, top-k) slot, grouped by expert in group
-// order, ascending slot within an expert: slot, tier code, token, expert id
+// decode pass record (int4), one per (token, top-k) slot, in slot order: slot, tier
+// code, token, expert id (written by the routing stage, read by the GEMVs)
 constexpr int kPassRec = 4;
 
 // Byte offsets of every scratch region (each 256-byte aligned).
 struct ScratchPlan {
   size_t topk_ids = 0, topk_w = 0, expert_tier = 0;
-  size_t d_counts = 0, d_experts = 0, d_nslots = 0, d_slots = 0, d_recs = 0, d_pass = 0;
+  size_t d_counts = 0, d_experts = 0, d_nslots = 0, d_slots = 0, d_pass = 0;
   size_t h_dec = 0, o_dec = 0;
   size_t a_counts = 0;                     // int32 [E] slot counts per expert
   size_t a_slots[2] = {0, 0}, a_bexp[2] = {0, 0}, a_eoff[2] = {0, 0}, a_npad[2] = {0, 0};

@@ -57,7 +57,6 @@ void plan_scratch(hmoe::Layer& L) {
   P.d_experts = take((size_t)L.max_distinct * 4);
   P.d_nslots = take((size_t)L.max_distinct * 4);
   P.d_slots = take((size_t)L.max_distinct * hmoe::kDecodeMaxM * 4);
-  P.d_recs = take((size_t)L.max_distinct * hmoe::kGroupRec * 4);
   P.d_pass = take(dec_slots * hmoe::kPassRec * 4);
   P.h_dec = take(dec_slots * L.I * 4);
   P.o_dec = take(dec_slots * L.H * 4);

@@ -1,6 +1,6 @@
 // Routing kernels: softmax top-k renormalised (one 64-lane wave per token), and the
-// decode variant that also writes the expert tier map and groups the M <= 8 tokens'
-// slots by distinct touched expert (the direct top-k addressing of the decode path,
+// decode variant that also writes each (token, top-k) slot's pass record and the
+// expert tier map (the direct top-k addressing of the decode path,
 // local-inference-lab/vllm PR #92, "How it works").
 #include <math.h>
 
@@ -36,10 +36,9 @@ __device__ __forceinline__ uint32_t order_key(float t) {
 // (sel_v, sel_id). Weights: softmax over the selected logits, in fp64, rounded once to
 // fp32.
 template <int NV>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
+__device__ __forceinline__ int route_token(const float* __restrict__ row, int E, int k, int lane,
                                             int32_t* __restrict__ ids_out,
-                                            float* __restrict__ w_out, int32_t* lds_ids,
-                                            TopkLds& tl) {
+                                            float* __restrict__ w_out, TopkLds& tl) {
   float v[NV];
   uint32_t u[NV];
 #pragma unroll
@@ -124,32 +123,20 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   if (lane < k) {
     ids_out[lane] = sel_id;
     w_out[lane] = (float)(ex / sum);
-    if (lds_ids) lds_ids[lane] = sel_id;
   }
+  return sel_id;
 }
 
-// route_token with NV = the smallest power of two covering E / 64 logits per lane
-__device__ __forceinline__ void route_token_any(const float* __restrict__ row, int E, int k,
-                                                int lane, int32_t* __restrict__ ids_out,
-                                                float* __restrict__ w_out, int32_t* lds_ids,
-                                                TopkLds& tl) {
-  if (E <= 64) route_token<1>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
-  else if (E <= 128) route_token<2>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
-  else if (E <= 256) route_token<4>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
-  else if (E <= 512) route_token<8>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
-  else route_token<16>(row, E, k, lane, ids_out, w_out, lds_ids, tl);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8 inside each
-// 16-lane row, then each row's total carried into the rows above (DPP row broadcasts).
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
-  return x;
+// route_token with NV = the smallest power of two covering E / 64 logits per lane; returns
+// lane j's selection (j < k)
+__device__ __forceinline__ int route_token_any(const float* __restrict__ row, int E, int k,
+                                               int lane, int32_t* __restrict__ ids_out,
+                                               float* __restrict__ w_out, TopkLds& tl) {
+  if (E <= 64) return route_token<1>(row, E, k, lane, ids_out, w_out, tl);
+  if (E <= 128) return route_token<2>(row, E, k, lane, ids_out, w_out, tl);
+  if (E <= 256) return route_token<4>(row, E, k, lane, ids_out, w_out, tl);
+  if (E <= 512) return route_token<8>(row, E, k, lane, ids_out, w_out, tl);
+  return route_token<16>(row, E, k, lane, ids_out, w_out, tl);
 }
 
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
@@ -160,126 +147,46 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
   const int t = blockIdx.x * kRouteWaves + (threadIdx.x >> 6);
   if (t >= M) return;
   route_token_any(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k,
-                  nullptr, tl[threadIdx.x >> 6]);
+                  tl[threadIdx.x >> 6]);
 }
 
-// Number of NF3-tier experts with id below 64 * chunk (the mask holds one bit per
-// expert, two words per 64-expert chunk).
-__device__ __forceinline__ int nf3_below_chunk(const TierMask& m, int chunk) {
+// Tier code of expert e (bit 16: NF3 tier; low 16 bits: index within its tier).
+__device__ __forceinline__ int tier_code(const TierMask& m, int e) {
   int below = 0;
-  for (int i = 0; i < 2 * chunk; ++i) below += __popc(m.w[i]);
-  return below;
+  for (int i = 0; i < (e >> 5); ++i) below += __popc(m.w[i]);
+  const uint32_t w = m.w[e >> 5];
+  below += __popc(w & ((1u << (e & 31)) - 1u));
+  return ((w >> (e & 31)) & 1u) ? ((1 << 16) | below) : (e - below);
 }
 
-struct RouteGroupArgs {
+struct RouteDecodeArgs {
   const float* logits;
-  int M, E, k, E4;
+  int M, E, k;
   int32_t* ids;
   float* w;
   int32_t* expert_tier;
-  int32_t* counts;     // [2]
-  int32_t* experts;    // [max_distinct]
-  int32_t* nslots;     // [max_distinct]
-  int32_t* slots;      // [max_distinct, 8]
-  int32_t* recs;       // [max_distinct, 16]: e, tier code, n, 0, slots[8], 0 x 4
-  int32_t* pass;       // [M * k, 4]: slot, tier code, token, e (grouped by expert)
+  int32_t* pass;  // [M * k, 4]: slot, tier code, token, e (slot order)
 };
 
 constexpr int kGroupThreads = kDecodeMaxM * kWave;  // one wave per decode token
 constexpr int kGroupWaves = kDecodeMaxM;
 
-__global__ __launch_bounds__(kGroupThreads) void route_group_kernel(RouteGroupArgs a, TierMask tm) {
-  __shared__ int32_t s_ids[kDecodeMaxM * kMaxTopK];
+// Decode routing (M <= 8): one wave per token; each slot's pass record (the direct
+// top-k addressing of the decode GEMVs) and the expert tier map. No block-wide step:
+// the distinct-expert grouping is built later, off the critical path, by the combine.
+__global__ __launch_bounds__(kGroupThreads) void route_decode_kernel(RouteDecodeArgs a, TierMask tm) {
   __shared__ TopkLds s_topk[kGroupWaves];
-  __shared__ uint32_t s_mask[kMaxExperts][4];   // slot bit masks (M * k <= 128 slots)
-  __shared__ int32_t s_order[kMaxExperts];      // (tier, local) position -> expert or -1
-  __shared__ int32_t s_pos[kMaxExperts];        // expert -> (tier, local) position
-  __shared__ int32_t s_d[kMaxExperts];          // expert -> group index
-  __shared__ int32_t s_tc[kMaxExperts];         // expert -> tier code
-  __shared__ int32_t s_poff[kMaxExperts];       // expert -> first pass record
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  if (wave < a.M)
-    route_token_any(a.logits + (size_t)wave * a.E, a.E, a.k, lane, a.ids + wave * a.k,
-                    a.w + wave * a.k, s_ids + wave * a.k, s_topk[wave]);
-  // tier map: one wave per 64-expert chunk, ranks by ballot
-  for (int chunk = wave; chunk * kWave < a.E; chunk += kGroupWaves) {
-    const int e = chunk * kWave + lane;
-    const bool in = e < a.E;
-    const bool nf3 = in && ((tm.w[e >> 5] >> (e & 31)) & 1u);
-    const uint64_t b = __ballot(nf3);
-    const int nf3_below = nf3_below_chunk(tm, chunk) + __popcll(b & lt);
-    if (in) {
-      const int32_t tc = nf3 ? ((1 << 16) | nf3_below) : (e - nf3_below);
-      a.expert_tier[e] = tc;
-      s_tc[e] = tc;
-      s_pos[e] = nf3 ? a.E4 + nf3_below : e - nf3_below;
-      s_mask[e][0] = s_mask[e][1] = s_mask[e][2] = s_mask[e][3] = 0u;
+  if (wave < a.M) {
+    const int e = route_token_any(a.logits + (size_t)wave * a.E, a.E, a.k, lane,
+                                  a.ids + wave * a.k, a.w + wave * a.k, s_topk[wave]);
+    if (lane < a.k) {
+      const int s = wave * a.k + lane;
+      reinterpret_cast<int4*>(a.pass)[s] = make_int4(s, tier_code(tm, e), wave, e);
     }
   }
-  __syncthreads();
-  const int nslot = a.M * a.k;
-  for (int s = threadIdx.x; s < nslot; s += kGroupThreads) {
-    const int e = s_ids[s];
-    if ((unsigned)e < (unsigned)a.E) atomicOr(&s_mask[e][s >> 5], 1u << (s & 31));
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < a.E; e += kGroupThreads) {
-    const bool touched = (s_mask[e][0] | s_mask[e][1] | s_mask[e][2] | s_mask[e][3]) != 0u;
-    s_order[s_pos[e]] = touched ? e : -1;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int running = 0, running_slots = 0;
-    int kept_distinct = 0;
-    for (int base = 0; base < a.E; base += kWave) {
-      const int pos = base + lane;
-      const int e = (pos < a.E) ? s_order[pos] : -1;
-      const bool f = e >= 0;
-      const uint64_t b = __ballot(f);
-      const int n = f ? __popc(s_mask[e][0]) + __popc(s_mask[e][1]) + __popc(s_mask[e][2]) +
-                            __popc(s_mask[e][3])
-                      : 0;
-      // inclusive scan of the slot counts over the wave: first pass record of each
-      const int incl = wave_incl_scan(n);
-      if (f) {
-        const int d = running + __popcll(b & lt);
-        s_d[e] = d;
-        s_poff[e] = running_slots + incl - n;
-        a.experts[d] = e;
-        a.nslots[d] = n < kDecodeMaxM ? n : kDecodeMaxM;
-        int4* rec = reinterpret_cast<int4*>(a.recs + d * kGroupRec);
-        rec[0] = make_int4(e, s_tc[e], n < kDecodeMaxM ? n : kDecodeMaxM, 0);
-        rec[3] = make_int4(0, 0, 0, 0);
-      }
-      const int cnt = __popcll(b);
-      if (base + kWave <= a.E4) kept_distinct += cnt;
-      else if (base < a.E4) kept_distinct += __popcll(b & ((1ull << (a.E4 - base)) - 1ull));
-      running += cnt;
-      running_slots += __builtin_amdgcn_readlane(incl, kWave - 1);
-    }
-    if (lane == 0) {
-      a.counts[0] = running;
-      a.counts[1] = kept_distinct;
-    }
-  }
-  __syncthreads();
-  // each slot lands at its rank among its expert's slots (ascending slot order)
-  for (int s = threadIdx.x; s < nslot; s += kGroupThreads) {
-    const int e = s_ids[s];
-    if ((unsigned)e >= (unsigned)a.E) continue;
-    int rank = 0;
-    for (int wd = 0; wd < (s >> 5); ++wd) rank += __popc(s_mask[e][wd]);
-    rank += __popc(s_mask[e][s >> 5] & ((1u << (s & 31)) - 1u));
-    if (rank < kDecodeMaxM) {
-      a.slots[s_d[e] * kDecodeMaxM + rank] = s;
-      a.recs[s_d[e] * kGroupRec + 4 + rank] = s;
-    }
-    const int p = s_poff[e] + rank;
-    if (p < nslot)
-      reinterpret_cast<int4*>(a.pass)[p] = make_int4(s, s_tc[e], s / a.k, e);
-  }
+  for (int e = threadIdx.x; e < a.E; e += kGroupThreads) a.expert_tier[e] = tier_code(tm, e);
 }
 
 hipError_t launch_route(const float* logits, int M, int E, int k, int32_t* ids, float* w,
@@ -294,22 +201,16 @@ hipError_t launch_route(const float* logits, int M, int E, int k, int32_t* ids, 
 hipError_t launch_route_group(const Layer& L, const float* logits, int M, void* scratch,
                               hipStream_t s) {
   char* base = static_cast<char*>(scratch);
-  RouteGroupArgs a;
+  RouteDecodeArgs a;
   a.logits = logits;
   a.M = M;
   a.E = L.E;
   a.k = L.k;
-  a.E4 = L.E4;
   a.ids = reinterpret_cast<int32_t*>(base + L.plan.topk_ids);
   a.w = reinterpret_cast<float*>(base + L.plan.topk_w);
   a.expert_tier = reinterpret_cast<int32_t*>(base + L.plan.expert_tier);
-  a.counts = reinterpret_cast<int32_t*>(base + L.plan.d_counts);
-  a.experts = reinterpret_cast<int32_t*>(base + L.plan.d_experts);
-  a.nslots = reinterpret_cast<int32_t*>(base + L.plan.d_nslots);
-  a.slots = reinterpret_cast<int32_t*>(base + L.plan.d_slots);
-  a.recs = reinterpret_cast<int32_t*>(base + L.plan.d_recs);
   a.pass = reinterpret_cast<int32_t*>(base + L.plan.d_pass);
-  hipLaunchKernelGGL(route_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, make_tier_mask(L));
+  hipLaunchKernelGGL(route_decode_kernel, dim3(1), dim3(kGroupThreads), 0, s, a, make_tier_mask(L));
   return hipGetLastError();
 }
 
