@@ -75,7 +75,7 @@ __device__ __forceinline__ int route_token(const float* __restrict__ row, int E,
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const uint64_t tie = __ballot(u[i] == tau);
-    const bool sel = u[i] > tau || (u[i] == tau && ties_before + __popcll(tie & lt) < need);
+    const bool sel = u[i] > tau || (u[i] == tau && ties_before + (int)__popcll(tie & lt) < need);
     const uint64_t sb = __ballot(sel);
     if (sel) {
       const int pos = placed + __popcll(sb & lt);
