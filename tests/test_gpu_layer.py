@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import synth
+from oracle import formats as F
 from oracle import layer as OL
 from hmoe_testlib import (check_output, make_layer, run_forward, scratch_for, tiny_packed,
                           to_dev, to_dev_bits, torch_mod)
@@ -51,6 +52,35 @@ def test_tiny_layer_wider_topk_and_experts(hm):
         lg = synth.router_logits(w, M)
         y, _ = run_forward(layer, wts, x, lg)
         check_output(y, OL.forward(packed, x, lg)["y"], f"E16 k4 M={M}")
+
+
+@pytest.mark.parametrize("kept,bit_map", [("nvfp4", "prefix"), ("mxfp4", "prefix"),
+                                           ("nvfp4", None)])
+def test_decode_shared_experts(hm, kept, bit_map):
+    """Decode with K a multiple of 512 (the matrix-core W13 path) in every kept format:
+    ordinary routing at M = 1, 3, 8, and routing forced onto the same four experts for
+    every token (each expert then serves all M = 8 tokens at once)."""
+    packed, w = tiny_packed(kept, bit_map, E=16, H=512, I=256, k=4, seed=5)
+    wts = hm.DeviceWeights(packed)
+    layer = make_layer(packed, 8)
+    # M = 1 has only 512 outputs, too few for the 1e-3 fraction bar on its own: the
+    # fraction is taken over the three batches together, the max bar per batch
+    ys, refs = [], []
+    for M in (1, 3, 8):
+        x = synth.activations_bf16(w, M)
+        lg = synth.router_logits(w, M)
+        y, _ = run_forward(layer, wts, x, lg)
+        ys.append(y.ravel())
+        refs.append(OL.forward(packed, x, lg)["y"].ravel())
+        yv = F.bf16_value(y.ravel()).astype(np.float64)
+        assert np.abs(yv - refs[-1]).max() <= 2e-2 * np.sqrt(np.mean(refs[-1] ** 2)), M
+    check_output(np.concatenate(ys), np.concatenate(refs), f"{kept} {bit_map} M=1,3,8")
+    x = synth.activations_bf16(w, 8)
+    lg = synth.router_logits(w, 8)
+    lg[:, [2, 5, 9, 12]] += 20.0  # experts 2 (kept) and 5, 9, 12 (tail) take every token
+    y, _ = run_forward(layer, wts, x, lg)
+    assert set(OL.route(lg, 4)[0].ravel().tolist()) == {2, 5, 9, 12}
+    check_output(y, OL.forward(packed, x, lg)["y"], f"{kept} {bit_map} shared experts")
 
 
 # ---------------------------------------------------------------- Qwen-shaped decode, full size
