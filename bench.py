@@ -241,6 +241,69 @@ def cpu_baseline(packed, x_bits, logits, budget_s=15.0, tokens=None):
                       f"elementwise work single-threaded"}
 
 
+def repack_bench(steps: int, warmup: int) -> dict:
+    """Times moe_repack (load-time demux of checkpoint-style per-expert tensors into the
+    tier-local arrays, NF3 code planes to the 3-bit stream) on the GLM-class layer with
+    random code bytes (a bit shuffle: its speed does not depend on the values)."""
+    import numpy as np
+    import torch
+    import synth
+    import weight_only_quantized_moe_amd as hm
+    w = synth.glm_decode()
+    bm = synth.bit_map(w)
+    E, H, I = w.E, w.H, w.I
+    layer = hm.moe_layer_create(E, H, I, w.top_k, 8, hm.KEPT_NVFP4, bm, 0)
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def rnd(n, dtype=torch.uint8):
+        return torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda", generator=g).view(dtype)
+
+    experts, src_bytes = [], 0
+    for e in range(E):
+        if bm[e] == 4:
+            ex = {"w13_q": rnd(2 * I * H // 2), "w13_s": rnd(2 * I * H // 16),
+                  "w13_g": torch.ones(1, dtype=torch.float32, device="cuda"),
+                  "w2_q": rnd(H * I // 2), "w2_s": rnd(H * I // 16),
+                  "w2_g": torch.ones(1, dtype=torch.float32, device="cuda")}
+        else:
+            ex = {"w13_lo": rnd(2 * I * H // 4), "w13_hi": rnd(2 * I * H // 8),
+                  "w13_s": rnd(2 * I * H // 32).view(torch.int16),
+                  "w2_lo": rnd(H * I // 4), "w2_hi": rnd(H * I // 8),
+                  "w2_s": rnd(H * I // 32).view(torch.int16)}
+        src_bytes += sum(t.numel() * t.element_size() for t in ex.values())
+        experts.append(ex)
+    empty = synth.empty_packed_layer(E, H, I, w.top_k, "nvfp4", bm)
+    dst = hm.DeviceWeights.__new__(hm.DeviceWeights)
+    dst.tensors = {}
+    for tier, keys in hm.DeviceWeights.KEYS.items():
+        for k in keys:
+            a = empty[tier][k]
+            dt = torch.int16 if a.dtype == np.uint16 else (torch.float32 if a.dtype == np.float32 else torch.uint8)
+            dst.tensors[f"{tier}_{k}"] = None if a.size == 0 else torch.empty(a.shape, dtype=dt, device="cuda")
+    dst._rebuild()
+    dst_bytes = dst.nbytes()
+    for _ in range(warmup):
+        hm.moe_repack(layer, experts, dst)
+    torch.cuda.synchronize()
+    s, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        hm.moe_repack(layer, experts, dst)
+    t.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(t) / steps
+    moved = src_bytes + dst_bytes
+    gbps = moved / (ms * 1e-3) / 1e9
+    return {"metric": "moe_repack GB/s (load-time demux + NF3 repack, bytes read + written)",
+            "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "u8", "data": "synthetic",
+            "config": {"workload": f"repack {describe(w, empty)}", "bytes_read": src_bytes,
+                       "bytes_written": dst_bytes},
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,6 +322,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=None,
                     help="prefill GEMM rows per expert block (16/32/64/128; default: the library picks "
                          "from max_tokens * top_k / E)")
+    ap.add_argument("--repack", action="store_true",
+                    help="time the load-time demux/repack (moe_repack) of the GLM-class layer "
+                         "instead of a forward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -271,6 +337,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+    if args.repack:
+        print(json.dumps(repack_bench(min(args.steps, 20), min(args.warmup, 2))))
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")

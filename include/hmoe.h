@@ -267,6 +267,40 @@ hmoe_status moe_dequant(const hmoe_layer* layer, const hmoe_weights* weights,
                         int32_t expert, int32_t tensor, float* out_f32, uint16_t* out_bf16,
                         hipStream_t stream);
 
+/* One expert's weight tensors as a checkpoint keeps them, addressed by global expert id
+ * (device pointers, owned by the caller, only read). The layer loader of the pages
+ * classifies experts by the bit map, loads each tier's tensors and repacks them into the
+ * kernels' formats ([P1] review walkthrough: the hybrid quant method's weight loading;
+ * [P2] "Summary": compact tier-local storage). Row layouts per expert:
+ *   kept tier: w13_q u8 [2I, H/2], w13_s u8 [2I, H/16] (E4M3) or [2I, H/32] (E8M0),
+ *              w13_g f32 [1] (NVFP4 only); w2_* likewise with [H, I/...];
+ *   NF3 tier:  w13_q = the low code plane u8 [2I, H/4] (element j at bits 2 (j mod 4)
+ *              of byte j / 4), w13_hi = the high plane u8 [2I, H/8] (element j at bit
+ *              j mod 8 of byte j / 8), code = low | high << 2; w13_s u16 [2I, H/64] fp16
+ *              bits; w2_* likewise with [H, I/...]. w13_g / w2_g are not read. */
+typedef struct hmoe_expert_src {
+    const uint8_t* w13_q;
+    const uint8_t* w13_hi;
+    const void* w13_s;
+    const float* w13_g;
+    const uint8_t* w2_q;
+    const uint8_t* w2_hi;
+    const void* w2_s;
+    const float* w2_g;
+} hmoe_expert_src;
+
+/* Load-time demux and repack: writes every expert of `experts` (host array of E
+ * entries, index = global expert id) into the tier-local arrays of `dst` (device
+ * pointers in the layouts of hmoe_weights, allocated by the caller): expert e goes to
+ * its tier at index = number of experts below e in the same tier; kept-tier tensors are
+ * copied, NF3 code planes become the 3-bit stream of the kernels. Asynchronous on
+ * `stream` (batched kernel launches, no allocation); source and destination must not
+ * overlap. Errors:
+ * HMOE_ERR_INVALID_ARG (null layer/experts/dst, a pointer the expert's tier needs is
+ * NULL, dst arrays of a non-empty tier NULL), HMOE_ERR_HIP. */
+hmoe_status moe_repack(const hmoe_layer* layer, const hmoe_expert_src* experts,
+                       const hmoe_weights* dst, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char* moe_status_string(hmoe_status status);
 

@@ -197,6 +197,36 @@ def unpack_nf3(packed: np.ndarray) -> np.ndarray:
     return out.reshape(lead + (nb // 3 * 8,))
 
 
+def pack_nf3_planes(q: np.ndarray):
+    """[N, K] codes 0..7 -> the two-plane NF3 layout a checkpoint may store (the
+    layout the survey of the pages proposed): a 2-bit low plane lo [N, K/4] with element
+    j at bits 2 (j mod 4) .. 2 (j mod 4) + 1 of byte j / 4, and a 1-bit high plane hi
+    [N, K/8] with element j at bit j mod 8 of byte j / 8; code = lo | hi << 2."""
+    q = np.asarray(q, dtype=np.uint32)
+    lead, K = q.shape[:-1], q.shape[-1]
+    u4 = (q & 3).reshape(lead + (K // 4, 4))
+    lo = np.zeros(lead + (K // 4,), dtype=np.uint32)
+    for i in range(4):
+        lo |= u4[..., i] << (2 * i)
+    u8 = (q >> 2).reshape(lead + (K // 8, 8))
+    hi = np.zeros(lead + (K // 8,), dtype=np.uint32)
+    for i in range(8):
+        hi |= (u8[..., i] & 1) << i
+    return lo.astype(np.uint8), hi.astype(np.uint8)
+
+
+def unpack_nf3_planes(lo: np.ndarray, hi: np.ndarray) -> np.ndarray:
+    lo = np.asarray(lo, dtype=np.uint8)
+    hi = np.asarray(hi, dtype=np.uint8)
+    lead, K = lo.shape[:-1], lo.shape[-1] * 4
+    out = np.empty(lead + (K,), dtype=np.uint8)
+    for j in range(4):
+        out[..., j::4] = (lo >> (2 * j)) & 3
+    for j in range(8):
+        out[..., j::8] |= ((hi >> j) & 1) << 2
+    return out
+
+
 # ----------------------------------------------------------------------------
 # dequantisation (fp32, the canonical values)
 # ----------------------------------------------------------------------------

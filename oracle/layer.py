@@ -209,3 +209,49 @@ def quantize_layer(E: int, H: int, I: int, top_k: int, bit_map, kept_format: str
             d["w13_q"][j], d["w13_s"][j] = F.nf3_quantize(w13)
             d["w2_q"][j], d["w2_s"][j] = F.nf3_quantize(w2)
     return layer
+
+
+# ----------------------------------------------------------------------------
+# checkpoint-style per-expert tensors and the load-time demux (tier-local arrays)
+# ----------------------------------------------------------------------------
+
+def checkpoint_experts(layer: dict):
+    """The layer as a checkpoint keeps it: one dict of tensors per global expert e.
+    Kept-tier experts hold their rows as the kept tier does (w13_q, w13_s, w13_g,
+    w2_q, w2_s, w2_g); NF3 experts hold two code planes per tensor (w13_lo, w13_hi,
+    w2_lo, w2_hi, see formats.pack_nf3_planes) and the fp16 group scales (w13_s, w2_s)."""
+    tier, local = tier_map(layer["bit_map"], layer["E"])
+    out = []
+    for e in range(layer["E"]):
+        j = int(local[e])
+        if tier[e] == KEPT:
+            k = layer["kept"]
+            out.append({n: np.array(k[n][j]) for n in ("w13_q", "w13_s", "w13_g", "w2_q", "w2_s", "w2_g")})
+        else:
+            f = layer["nf3"]
+            d = {}
+            for t in ("w13", "w2"):
+                d[t + "_lo"], d[t + "_hi"] = F.pack_nf3_planes(F.unpack_nf3(f[t + "_q"][j]))
+                d[t + "_s"] = np.array(f[t + "_s"][j])
+            out.append(d)
+    return out
+
+
+def demux(experts, bit_map, E: int, H: int, I: int, top_k: int, kept_format: str):
+    """Tier-local arrays from checkpoint-style experts: each expert goes to its tier at
+    its tier-local index (experts below it in the same tier, ascending global id); NF3
+    code planes become the 3-bit stream of the kernels. The inverse of
+    checkpoint_experts."""
+    from synth import empty_packed_layer
+    layer = empty_packed_layer(E, H, I, top_k, kept_format, bit_map)
+    tier, local = tier_map(bit_map, E)
+    for e in range(E):
+        j, src = int(local[e]), experts[e]
+        if tier[e] == KEPT:
+            for n in ("w13_q", "w13_s", "w13_g", "w2_q", "w2_s", "w2_g"):
+                layer["kept"][n][j] = src[n]
+        else:
+            for t in ("w13", "w2"):
+                layer["nf3"][t + "_q"][j] = F.pack_nf3(F.unpack_nf3_planes(src[t + "_lo"], src[t + "_hi"]))
+                layer["nf3"][t + "_s"][j] = src[t + "_s"]
+    return layer

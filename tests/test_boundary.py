@@ -141,3 +141,16 @@ def test_forward_argument_errors_without_launching():
     assert lib.moe_dequant(layer.handle, ctypes.byref(w), 8, 0, ctypes.c_void_p(a), None, None) == INVALID
     assert lib.moe_dequant(layer.handle, ctypes.byref(w), 0, 2, ctypes.c_void_p(a), None, None) == INVALID
     assert lib.moe_dequant(layer.handle, ctypes.byref(w), 0, 0, None, None, None) == INVALID
+
+
+def test_repack_argument_errors_without_launching():
+    """moe_repack validates on the host before any copy: a NULL expert table or NULL
+    destination arrays of a non-empty tier are argument errors."""
+    lib = hm.load_library()
+    layer = hm.moe_layer_create(8, 256, 128, 2, 16, hm.KEPT_NVFP4,
+                                np.array([4, 4, 3, 3, 4, 3, 4, 3], np.uint8), 0)
+    w = hm.Weights()
+    assert lib.moe_repack(layer.handle, None, ctypes.byref(w), None) == INVALID
+    src = (hm.ExpertSrc * 8)()
+    assert lib.moe_repack(layer.handle, src, ctypes.byref(w), None) == INVALID
+    assert lib.moe_repack(None, src, ctypes.byref(w), None) == INVALID

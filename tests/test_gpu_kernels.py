@@ -192,3 +192,56 @@ def test_align_bit_exact(hm, E, k, M, bm, n_kept):
         assert np.array_equal(v["sorted_slots"].cpu().numpy()[:npad], ref[t]["sorted_slots"])
         assert np.array_equal(v["block_expert"].cpu().numpy()[: npad // bm], ref[t]["block_expert"])
         assert np.array_equal(v["expert_off"].cpu().numpy(), ref[t]["expert_off"])
+
+
+# ---------------------------------------------------------------- load-time demux / repack
+
+def _repack_case(kept, rule, E, H, I, k, n_kept, seed):
+    w = synth.Workload("repack", E, H, I, k, 4, kept, n_kept, rule, seed=seed)
+    bm = synth.bit_map(w)
+    packed = OL.quantize_layer(E, H, I, k, bm, kept, lambda e: synth.master_weights(w, e))
+    return packed, w
+
+
+@pytest.mark.parametrize("kept,rule,E,H,I,k,n_kept", [
+    ("nvfp4", "prefix", 8, 256, 128, 2, 4),
+    ("mxfp4", "prefix", 8, 256, 128, 2, 4),
+    ("nvfp4", "none", 8, 256, 128, 2, None),
+    ("mxfp4", "random", 16, 512, 256, 4, 5),
+    ("nvfp4", "random", 16, 512, 256, 4, 11),
+])
+def test_repack_bit_exact(hm, kept, rule, E, H, I, k, n_kept):
+    """moe_repack of checkpoint-style per-expert tensors (NF3 codes as two planes)
+    reproduces the oracle's tier-local arrays byte for byte, and a forward on the
+    repacked weights equals the forward on the original ones bit for bit."""
+    torch = torch_mod()
+    packed, w = _repack_case(kept, rule, E, H, I, k, n_kept, seed=9)
+    ckpt = OL.checkpoint_experts(packed)
+    dev = []
+    for ex in ckpt:
+        dev.append({n: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16
+                                        else np.ascontiguousarray(a).reshape(-1)).cuda()
+                    for n, a in ex.items()})
+    empty = synth.empty_packed_layer(E, H, I, k, packed["kept_format"], packed["bit_map"])
+    dst = hm.DeviceWeights(empty)
+    layer = make_layer(packed, 32)
+    hm.moe_repack(layer, dev, dst)
+    torch.cuda.synchronize()
+    for tier, keys in hm.DeviceWeights.KEYS.items():
+        for key in keys:
+            t = dst.tensors[f"{tier}_{key}"]
+            ref = packed[tier][key]
+            if t is None:
+                assert ref.size == 0
+                continue
+            got = t.cpu().numpy()
+            if ref.dtype == np.uint16:
+                got = got.view(np.uint16)
+            assert np.array_equal(got.reshape(ref.shape), ref), (tier, key)
+    orig = hm.DeviceWeights(packed)
+    for M in (3, 20):
+        x = synth.activations_bf16(w, M)
+        lg = synth.router_logits(w, M)
+        y1, _ = run_forward(layer, orig, x, lg)
+        y2, _ = run_forward(layer, dst, x, lg)
+        assert np.array_equal(y1, y2), M

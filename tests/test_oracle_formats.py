@@ -281,3 +281,27 @@ def test_dequant_closed_forms():
     # NF3: level 7 (1.0) times fp16 scale 0.5
     q = F.pack_nf3(np.array([[7] + [3] * 63]))
     assert F.nf3_dequant(q, np.array([[0x3800]], np.uint16))[0, 0] == 0.5
+
+
+# ---------------------------------------------------------------- NF3 checkpoint planes
+
+def test_nf3_planes_hand_bit_positions():
+    """Element j alone at code c: the low plane holds c & 3 at bits 2 (j mod 4) of byte
+    j / 4, the high plane c >> 2 at bit j mod 8 of byte j / 8."""
+    K = 64
+    for j in (0, 3, 4, 7, 8, 13, 31, 63):
+        for c in (1, 2, 3, 4, 5, 7):
+            q = np.zeros((1, K), dtype=np.uint8)
+            q[0, j] = c
+            lo, hi = F.pack_nf3_planes(q)
+            exp_lo = np.zeros(K // 4, dtype=np.uint8)
+            exp_lo[j // 4] = (c & 3) << (2 * (j % 4))
+            exp_hi = np.zeros(K // 8, dtype=np.uint8)
+            exp_hi[j // 8] = (c >> 2) << (j % 8)
+            assert np.array_equal(lo[0], exp_lo) and np.array_equal(hi[0], exp_hi), (j, c)
+            assert np.array_equal(F.unpack_nf3_planes(lo, hi), q)
+
+
+def test_nf3_planes_round_trip_random():
+    q = np.random.default_rng(7).integers(0, 8, (3, 4, 192)).astype(np.uint8)
+    assert np.array_equal(F.unpack_nf3_planes(*F.pack_nf3_planes(q)), q)

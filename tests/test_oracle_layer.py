@@ -208,3 +208,39 @@ def test_mxfp4_kept_tier_layer_runs():
     # MXFP4 dequant tracks the master weights to within the E2M1 grid step
     assert np.max(np.abs(w13 - master13)) < 0.25 * np.abs(master13).max()
     assert np.all(np.isfinite(out["y"]))
+
+
+# ---------------------------------------------------------------- load-time demux
+
+def test_demux_places_each_expert_by_brute_force():
+    """Tier-local index of expert e = number of experts below e in e's tier; the NF3
+    stream of a demuxed expert equals the stream packing of its plane codes."""
+    from hmoe_testlib import tiny_packed
+    packed, _ = tiny_packed("mxfp4", "prefix", E=8, H=256, I=128, k=2, seed=4)
+    E = packed["E"]
+    bm = np.array([3, 4, 3, 3, 4, 4, 3, 4], dtype=np.uint8)  # irregular map
+    # a layer with this map whose expert e carries data tagged by e
+    experts = L.checkpoint_experts(packed)
+    kept_src = [e for e in range(E) if packed["bit_map"][e] == 4]
+    nf3_src = [e for e in range(E) if packed["bit_map"][e] == 3]
+    pool = {4: [experts[e] for e in kept_src], 3: [experts[e] for e in nf3_src]}
+    mine = []
+    used = {3: 0, 4: 0}
+    for e in range(E):
+        b = int(bm[e])
+        mine.append(pool[b][used[b] % len(pool[b])])
+        used[b] += 1
+    layer = L.demux(mine, bm, E, packed["H"], packed["I"], packed["top_k"], "mxfp4")
+    for e in range(E):
+        same = [x for x in range(e) if bm[x] == bm[e]]
+        j = len(same)
+        if bm[e] == 4:
+            assert np.array_equal(layer["kept"]["w13_q"][j], mine[e]["w13_q"])
+            assert np.array_equal(layer["kept"]["w2_s"][j], mine[e]["w2_s"])
+        else:
+            q = F.unpack_nf3_planes(mine[e]["w2_lo"], mine[e]["w2_hi"])
+            assert np.array_equal(F.unpack_nf3(layer["nf3"]["w2_q"][j]), q)
+            assert np.array_equal(layer["nf3"]["w13_s"][j], mine[e]["w13_s"])
+    back = L.checkpoint_experts(layer)
+    for e in range(E):
+        assert set(back[e]) == set(mine[e]) and all(np.array_equal(back[e][k], mine[e][k]) for k in mine[e])

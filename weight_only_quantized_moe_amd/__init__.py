@@ -27,7 +27,8 @@ DECODE_MAX_M = 8
 EXPORTED = (
     "moe_layer_create", "moe_layer_destroy", "moe_layer_query", "moe_scratch_bytes",
     "moe_route", "moe_align", "moe_align_view", "moe_decode_view", "moe_topk_view",
-    "hybrid_moe_forward", "hybrid_moe_forward_stage", "moe_dequant", "moe_status_string", "moe_last_error",
+    "hybrid_moe_forward", "hybrid_moe_forward_stage", "moe_dequant", "moe_repack",
+    "moe_status_string", "moe_last_error",
 )
 
 
@@ -53,6 +54,11 @@ class Weights(Structure):
     _fields_ = [(n, c_void_p) for n in (
         "kept_w13_q", "kept_w13_s", "kept_w13_g", "kept_w2_q", "kept_w2_s", "kept_w2_g",
         "nf3_w13_q", "nf3_w13_s", "nf3_w2_q", "nf3_w2_s")]
+
+
+class ExpertSrc(Structure):
+    _fields_ = [(n, c_void_p) for n in (
+        "w13_q", "w13_hi", "w13_s", "w13_g", "w2_q", "w2_hi", "w2_s", "w2_g")]
 
 
 class AlignView(Structure):
@@ -106,6 +112,8 @@ def load_library() -> ctypes.CDLL:
     lib.moe_dequant.argtypes = [c_void_p, POINTER(Weights), c_int32, c_int32, c_void_p, c_void_p,
                                 c_void_p]
     lib.moe_dequant.restype = st
+    lib.moe_repack.argtypes = [c_void_p, POINTER(ExpertSrc), POINTER(Weights), c_void_p]
+    lib.moe_repack.restype = st
     lib.moe_status_string.argtypes = [c_int32]
     lib.moe_status_string.restype = c_char_p
     lib.moe_last_error.argtypes = []
@@ -262,6 +270,21 @@ def moe_dequant(layer: Layer, weights: "DeviceWeights", expert: int, tensor: int
                 out_f32=None, out_bf16=None, stream=None) -> None:
     _check(load_library().moe_dequant(layer.handle, byref(weights.struct), expert, tensor,
                                       _ptr(out_f32), _ptr(out_bf16), _stream(stream)))
+
+
+def moe_repack(layer: Layer, experts, dst: "DeviceWeights", stream=None) -> None:
+    """Load-time demux/repack (include/hmoe.h): `experts` is a list of E dicts of device
+    tensors in the checkpoint layout (kept tier: w13_q, w13_s, w13_g, w2_q, w2_s, w2_g;
+    NF3 tier: w13_lo, w13_hi, w13_s, w2_lo, w2_hi, w2_s), written into the tier-local
+    arrays of `dst`."""
+    arr = (ExpertSrc * len(experts))()
+    for i, ex in enumerate(experts):
+        nf3 = "w13_lo" in ex
+        arr[i] = ExpertSrc(
+            _ptr(ex["w13_lo"] if nf3 else ex["w13_q"]), _ptr(ex.get("w13_hi")), _ptr(ex["w13_s"]),
+            _ptr(ex.get("w13_g")), _ptr(ex["w2_lo"] if nf3 else ex["w2_q"]), _ptr(ex.get("w2_hi")),
+            _ptr(ex["w2_s"]), _ptr(ex.get("w2_g")))
+    _check(load_library().moe_repack(layer.handle, arr, byref(dst.struct), _stream(stream)))
 
 
 class DeviceWeights:

@@ -83,6 +83,26 @@ hipError_t launch_prefill_x16(const Layer& L, const uint16_t* x, int M, void* sc
 hipError_t launch_dequant(const Layer& L, const hmoe_weights& W, int expert, int tensor,
                           float* out_f32, uint16_t* out_bf16, hipStream_t s);
 
+// repack.hip: a batch of copy jobs (n bytes) and NF3 plane-to-stream jobs (n units of
+// 32 elements: src = low plane, src_hi = high plane, dst = stream), one launch
+constexpr int kRepackThreads = 256;
+constexpr int kRepackJobs = 24;
+enum : int { kRepackCopy = 0, kRepackNf3 = 1 };
+struct RepackJob {
+  const void* src;
+  const void* src_hi;
+  void* dst;
+  long n;
+  int kind;
+  int blocks;
+};
+struct RepackBatch {
+  RepackJob job[kRepackJobs];
+  int first_block[kRepackJobs];
+  int njobs;
+};
+hipError_t launch_repack(RepackBatch& b, hipStream_t s);
+
 TierMask make_tier_mask(const Layer& L);
 
 bool plan_gemv(int K, GemvTiling* t);

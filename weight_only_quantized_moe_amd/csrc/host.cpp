@@ -369,6 +369,79 @@ hmoe_status moe_dequant(const hmoe_layer* layer, const hmoe_weights* weights, in
   return HMOE_OK;
 }
 
+hmoe_status moe_repack(const hmoe_layer* layer, const hmoe_expert_src* experts,
+                       const hmoe_weights* dst, hipStream_t stream) {
+  if (hmoe_status st = check_layer(layer)) return st;
+  const hmoe::Layer& L = layer->L;
+  if (!experts) return fail(HMOE_ERR_INVALID_ARG, "experts is NULL");
+  if (hmoe_status st = check_weights(L, dst)) return st;
+  const bool nv = L.kept_format == HMOE_KEPT_NVFP4;
+  struct Tensor {
+    long rows;
+    int K;
+  };
+  const Tensor ts[2] = {{2L * L.I, L.H}, {(long)L.H, L.I}};
+  // validate every expert before the first copy
+  for (int e = 0; e < L.E; ++e) {
+    const hmoe_expert_src& s = experts[e];
+    const bool nf3 = (L.nf3_mask[e >> 5] >> (e & 31)) & 1u;
+    if (!s.w13_q || !s.w13_s || !s.w2_q || !s.w2_s)
+      return fail(HMOE_ERR_INVALID_ARG, "expert " + std::to_string(e) + ": a code or scale pointer is NULL");
+    if (nf3 && (!s.w13_hi || !s.w2_hi))
+      return fail(HMOE_ERR_INVALID_ARG, "NF3 expert " + std::to_string(e) + ": a high code plane is NULL");
+    if (nf3 && (!aligned(s.w13_q, 4) || !aligned(s.w13_hi, 4) || !aligned(s.w2_q, 4) ||
+                !aligned(s.w2_hi, 4)))
+      return fail(HMOE_ERR_ALIGN, "NF3 expert " + std::to_string(e) + ": code planes need 4-byte alignment");
+    if (!nf3 && nv && (!s.w13_g || !s.w2_g))
+      return fail(HMOE_ERR_INVALID_ARG, "NVFP4 expert " + std::to_string(e) + ": a per-tensor scale is NULL");
+  }
+  uint8_t* kq[2] = {const_cast<uint8_t*>(dst->kept_w13_q), const_cast<uint8_t*>(dst->kept_w2_q)};
+  uint8_t* ks[2] = {const_cast<uint8_t*>(dst->kept_w13_s), const_cast<uint8_t*>(dst->kept_w2_s)};
+  float* kg[2] = {const_cast<float*>(dst->kept_w13_g), const_cast<float*>(dst->kept_w2_g)};
+  uint8_t* nq[2] = {const_cast<uint8_t*>(dst->nf3_w13_q), const_cast<uint8_t*>(dst->nf3_w2_q)};
+  uint16_t* ns[2] = {const_cast<uint16_t*>(dst->nf3_w13_s), const_cast<uint16_t*>(dst->nf3_w2_s)};
+  int below[2] = {0, 0};  // experts of each tier so far: the tier-local index
+  hmoe::RepackBatch batch{};
+  auto add = [&](const void* src, const void* hi, void* out, long n, int kind) -> hipError_t {
+    batch.job[batch.njobs++] = {src, hi, out, n, kind, 0};
+    if (batch.njobs < hmoe::kRepackJobs) return hipSuccess;
+    hipError_t err = hmoe::launch_repack(batch, stream);
+    batch.njobs = 0;
+    return err;
+  };
+  for (int e = 0; e < L.E; ++e) {
+    const hmoe_expert_src& s = experts[e];
+    const int tier = ((L.nf3_mask[e >> 5] >> (e & 31)) & 1u) ? 1 : 0;
+    const long loc = below[tier]++;
+    const uint8_t* sq[2] = {s.w13_q, s.w2_q};
+    const uint8_t* shi[2] = {s.w13_hi, s.w2_hi};
+    const void* ss[2] = {s.w13_s, s.w2_s};
+    const float* sg[2] = {s.w13_g, s.w2_g};
+    for (int t = 0; t < 2; ++t) {
+      const long rows = ts[t].rows;
+      const int K = ts[t].K;
+      hipError_t err = hipSuccess;
+      if (tier == 0) {
+        const long qb = rows * (K / 2), sb = rows * (K / (nv ? 16 : 32));
+        err = add(sq[t], nullptr, kq[t] + loc * qb, qb, hmoe::kRepackCopy);
+        if (err == hipSuccess) err = add(ss[t], nullptr, ks[t] + loc * sb, sb, hmoe::kRepackCopy);
+        if (err == hipSuccess && nv && kg[t])
+          err = add(sg[t], nullptr, kg[t] + loc, (long)sizeof(float), hmoe::kRepackCopy);
+      } else {
+        const long qb = rows * (3L * K / 8), sn = rows * (K / 64);
+        err = add(sq[t], shi[t], nq[t] + loc * qb, rows * (K / 32), hmoe::kRepackNf3);
+        if (err == hipSuccess) err = add(ss[t], nullptr, ns[t] + loc * sn, sn * 2, hmoe::kRepackCopy);
+      }
+      if (err != hipSuccess) return hip_fail(err, "repack");
+    }
+  }
+  if (batch.njobs > 0) {
+    hipError_t err = hmoe::launch_repack(batch, stream);
+    if (err != hipSuccess) return hip_fail(err, "repack");
+  }
+  return HMOE_OK;
+}
+
 const char* moe_status_string(hmoe_status s) {
   switch (s) {
     case HMOE_OK: return "HMOE_OK";
