@@ -13,21 +13,30 @@
 
 namespace hmoe {
 
+// Eight elements: x holds their low code bits (element i at bits 2i..2i+1), h their
+// high bits (element i at bit i); returns the 24-bit stream (element i at bits 3i..3i+2).
+// Each 2-bit field moves up by i and each high bit by 2i + 2, done as three masked
+// moves by 4, 2 and 1 (2i: 8, 4, 2), the largest first so no field lands on another.
+__device__ __forceinline__ uint32_t nf3_spread8(uint32_t x, uint32_t h) {
+  uint32_t t = (x & 0x00FFu) | ((x & 0xFF00u) << 4);       // fields 4..7 up by 4
+  t = (t & ~0x000F00F0u) | ((t & 0x000F00F0u) << 2);       // fields 2, 3, 6, 7 up by 2
+  t = (t & ~0x0030C30Cu) | ((t & 0x0030C30Cu) << 1);       // fields 1, 3, 5, 7 up by 1
+  uint32_t u = (h & 0x0Fu) | ((h & 0xF0u) << 8);            // bits 4..7 up by 8
+  u = (u & ~0x0000C00Cu) | ((u & 0x0000C00Cu) << 4);        // bits 2, 3, 6, 7 up by 4
+  u = (u & ~0x00082082u) | ((u & 0x00082082u) << 2);        // bits 1, 3, 5, 7 up by 2
+  return t | (u << 2);
+}
+
 // 32-element NF3 units: 8 low-plane bytes and 4 high-plane bytes in, 12 stream bytes out
 __device__ __forceinline__ void nf3_unit(const uint32_t* lo, const uint32_t* hi, uint32_t* out, long u) {
   const uint32_t l0 = lo[2 * u], l1 = lo[2 * u + 1], h = hi[u];
-  uint32_t s[3] = {0u, 0u, 0u};
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t lw = j < 16 ? l0 : l1;
-    const uint32_t q = ((lw >> (2 * (j & 15))) & 3u) | (((h >> j) & 1u) << 2);
-    const int b = 3 * j;  // bit position in the 96-bit unit
-    s[b >> 5] |= q << (b & 31);
-    if ((b & 31) > 29) s[(b >> 5) + 1] |= q >> (32 - (b & 31));
-  }
-  out[3 * u] = s[0];
-  out[3 * u + 1] = s[1];
-  out[3 * u + 2] = s[2];
+  const uint32_t g0 = nf3_spread8(l0 & 0xFFFFu, h & 0xFFu);
+  const uint32_t g1 = nf3_spread8(l0 >> 16, (h >> 8) & 0xFFu);
+  const uint32_t g2 = nf3_spread8(l1 & 0xFFFFu, (h >> 16) & 0xFFu);
+  const uint32_t g3 = nf3_spread8(l1 >> 16, h >> 24);
+  out[3 * u] = g0 | (g1 << 24);
+  out[3 * u + 1] = (g1 >> 8) | (g2 << 16);
+  out[3 * u + 2] = (g2 >> 16) | (g3 << 8);
 }
 
 __global__ __launch_bounds__(kRepackThreads) void repack_kernel(RepackBatch b) {
