@@ -185,3 +185,22 @@ def test_glm_prefill_m4096_sampled(hm):
 def test_glm_mxfp4_m512_and_uniform_control(hm):
     _glm_case(hm, synth.glm_mxfp4(512), [0, 511])
     _glm_case(hm, synth.glm_uniform(512), [7])
+
+
+# ---------------------------------------------------------------- maximum sizes, empty tier
+
+@pytest.mark.parametrize("rule,n_kept", [("random", 300), ("prefix", 0)])
+def test_max_experts_and_topk(hm, rule, n_kept):
+    """The library's largest expert count (1024) and top-k (16) through decode (M = 1, 8)
+    and prefill (M = 9, 64), with a random 300-expert kept tier, and with the kept tier
+    empty (every expert NF3: the kept arrays are NULL)."""
+    w = synth.Workload("max", 1024, 256, 128, 16, 64, "nvfp4", n_kept, rule, seed=11)
+    packed = synth.packed_layer(w)
+    assert packed["kept"]["w13_q"].shape[0] == n_kept
+    wts = hm.DeviceWeights(packed)
+    layer = make_layer(packed, 64)
+    for M in (1, 8, 9, 64):
+        x = synth.activations_bf16(w, M)
+        lg = synth.router_logits(w, M)
+        y, _ = run_forward(layer, wts, x, lg)
+        check_output(y, OL.forward(packed, x, lg)["y"], f"E=1024 k=16 {rule} M={M}")
