@@ -68,13 +68,18 @@ __device__ __forceinline__ float seg_reduce(const float (&v)[V]) {
   } else {
     constexpr int H = V / 2;
     constexpr int off = LR / 2;
-    const bool hi = (threadIdx.x & off) != 0;
     float nv[H];
+    if constexpr (off == 32 || off == 16) {
 #pragma unroll
-    for (int j = 0; j < H; ++j) {
-      const float keep = hi ? v[j + H] : v[j];
-      const float send = hi ? v[j] : v[j + H];
-      nv[j] = keep + xlane<off>(send);
+      for (int j = 0; j < H; ++j) nv[j] = swap_add<off>(v[j], v[j + H]);
+    } else {
+      const bool hi = (threadIdx.x & off) != 0;
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const float keep = hi ? v[j + H] : v[j];
+        const float send = hi ? v[j] : v[j + H];
+        nv[j] = keep + xlane<off>(send);
+      }
     }
     return seg_reduce<H, LR / 2>(nv);
   }
@@ -339,18 +344,62 @@ struct W13Buf {
   uint32_t sg[RI][KU], su[RI][KU];
 };
 
+// Buffer resources of one expert's codes and scales: a load then takes the chunk's row
+// offset in a scalar register and the lane's fixed offset in a vector register, so no
+// vector instruction computes addresses inside the loop.
+struct ExpertRsrc {
+  __amdgpu_buffer_rsrc_t q, s;
+};
+
+template <int FMT>
+__device__ __forceinline__ ExpertRsrc expert_rsrc(const GemvArgs& a, int loc) {
+  const int RB = FMT == kFmtNf3 ? 3 * a.K / 8 : a.K / 2;
+  const int SB = FMT == kFmtNvfp4 ? a.K / 16 : a.K / 32;
+  const uint8_t* q = (FMT == kFmtNf3 ? a.nq : a.kq) + (size_t)loc * a.rows * RB;
+  const uint8_t* s = (FMT == kFmtNf3 ? reinterpret_cast<const uint8_t*>(a.ns) : a.ks) +
+                     (size_t)loc * a.rows * SB;
+  return {__builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(q), 0, a.rows * RB, 0x00020000),
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(s), 0, a.rows * SB, 0x00020000)};
+}
+
+// one row's KU units (codes + scale word) for this lane: row = uniform row of the
+// expert, rw = this lane's row within the load
+template <int LR, int KU, int FMT>
+__device__ __forceinline__ void load_row_rsrc(const ExpertRsrc& r, int K, int row, int rw, int c,
+                                              uint4 (&q)[KU], uint32_t (&sc)[KU]) {
+  const int RB = FMT == kFmtNf3 ? 3 * K / 8 : K / 2;
+  const int SB = FMT == kFmtNvfp4 ? K / 16 : K / 32;
+#pragma unroll
+  for (int j = 0; j < KU; ++j) {
+    const int u = c + LR * j;
+    if constexpr (FMT == kFmtNf3) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b96(r.q, rw * RB + 12 * u, row * RB, 0);
+      q[j] = make_uint4(v[0], v[1], v[2], 0u);
+      sc[j] = __builtin_amdgcn_raw_buffer_load_b16(r.s, rw * SB + 2 * (u >> 1), row * SB, 0);
+    } else if constexpr (FMT == kFmtNvfp4) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r.q, rw * RB + 16 * u, row * RB, 0);
+      q[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      sc[j] = __builtin_amdgcn_raw_buffer_load_b16(r.s, rw * SB + 2 * u, row * SB, 0);
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r.q, rw * RB + 16 * u, row * RB, 0);
+      q[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      sc[j] = __builtin_amdgcn_raw_buffer_load_b8(r.s, rw * SB + u, row * SB, 0);
+    }
+  }
+}
+
 template <int LR, int KU, int RI, int FMT>
 __device__ __forceinline__ void w13_load(const GemvArgs& a, int loc, int i0, W13Buf<KU, RI>& b) {
   constexpr int P = kWave / LR;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % LR;
   const int rw = lane / LR;
-  const size_t base = (size_t)loc * a.rows;
+  const ExpertRsrc r = expert_rsrc<FMT>(a, loc);
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
-    const int i = i0 + ri * P + rw;
-    load_row<LR, KU, FMT>(a, base + i, c, b.qg[ri], b.sg[ri]);
-    load_row<LR, KU, FMT>(a, base + a.I + i, c, b.qu[ri], b.su[ri]);
+    const int i = i0 + ri * P;
+    load_row_rsrc<LR, KU, FMT>(r, a.K, i, rw, c, b.qg[ri], b.sg[ri]);
+    load_row_rsrc<LR, KU, FMT>(r, a.K, a.I + i, rw, c, b.qu[ri], b.su[ri]);
   }
 }
 
@@ -514,6 +563,7 @@ __device__ __forceinline__ void w2_load(const GemvArgs& a, int loc, int n0, W2Bu
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % LR;
   const int rw = lane / LR;
+  // flat loads here: buffer loads made the W2 GEMV slower on the GLM-class layer
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri)
     load_row<LR, KU, FMT>(a, (size_t)loc * a.rows + n0 + ri * P + rw, c, b.q[ri], b.sc[ri]);

@@ -192,11 +192,27 @@ __device__ __forceinline__ double xlane_d(double v) {
   return __builtin_bit_cast(double, lo | (hi << 32));
 }
 
+// a + b across lane halves (B = 32) or rows (B = 16) in two operations: after one
+// v_permlane32_swap (v_permlane16_swap) of (a, b), the two results hold, lane by lane,
+// the own and the partner lane's values of a for lanes with bit B clear and of b for lanes
+// with bit B set; their sum is a[l] + a[l ^ B] (bit B clear) or b[l] + b[l ^ B] (set)
+template <int B>
+__device__ __forceinline__ float swap_add(float a, float b) {
+  static_assert(B == 16 || B == 32, "swap distance");
+  if constexpr (B == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 // sum / max over aligned WIDTH-lane groups (every lane of the group gets the result)
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (WIDTH >= 64) v += xlane<32>(v);
-  if constexpr (WIDTH >= 32) v += xlane<16>(v);
+  if constexpr (WIDTH >= 64) v = swap_add<32>(v, v);
+  if constexpr (WIDTH >= 32) v = swap_add<16>(v, v);
   if constexpr (WIDTH >= 16) v += xlane<8>(v);
   if constexpr (WIDTH >= 8) v += xlane<4>(v);
   if constexpr (WIDTH >= 4) v += xlane<2>(v);
