@@ -6,6 +6,8 @@
 //
 // GEMM: a block computes BM slots x 128 weight rows (W13: 64 gate rows and the
 // matching 64 up rows; W2: 128 output columns) over K in steps of 64 (one NF3 group),
+// BM being the smallest of 16, 32, 64 and block_m rows that holds the real slots of
+// its block_m-row align block (so an expert's last, partly padded block costs less),
 // with fp16 16x16x32 MFMAs. Four waves split the tile 2 x 2 (1 x 4 for BM = 16). LDS
 // holds two stages of the activation and the decoded weight tile: while one stage
 // feeds the MFMAs, the next step's raw weights and activations are already in
@@ -144,7 +146,7 @@ __device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32
 // VS: the weight scales of 8 consecutive steps of a row are one aligned 16-byte vector
 // (two for NVFP4) and are loaded 8 steps at a time; otherwise one load per step.
 template <int BM, bool W13, int FMT, bool VS>
-__device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b, int loc, int tile,
+__device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int r0, int loc, int tile,
                                           GemmSmem<BM>& sm) {
   using S = GemmShape<BM, W13>;
   constexpr int MT = S::MT, NT = S::NT;
@@ -156,8 +158,8 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
   const int j = lane & 15, g = lane >> 4;
   const int n0 = tile * (W13 ? kBN / 2 : kBN);
-  const int32_t* bslots = a.slots[tier] + (size_t)b * BM;
-  const size_t hbase = (size_t)(tier ? a.hrow1 : 0) + (size_t)b * BM;
+  const int32_t* bslots = a.slots[tier] + r0;
+  const size_t hbase = (size_t)(tier ? a.hrow1 : 0) + r0;
   const int steps = a.K / kBK;
 
   // ---- weight units. Thread (wave w, lane l) owns tile rows rA = 32 w + (l >> 2) and
@@ -522,7 +524,30 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int b,
   }
 }
 
-template <int BM, bool W13>
+// One tile of BMC slot rows at row r0 (BMC <= BMAX), in the format of its tier and the
+// layer's scale layout.
+template <int BMC, int BMAX, bool W13>
+__device__ __forceinline__ void gemm_tile_any(const PrefillArgs& a, int tier, int r0, int loc, int tile,
+                                              unsigned char* smem) {
+  static_assert(sizeof(GemmSmem<BMC>) <= sizeof(GemmSmem<BMAX>), "tile class larger than its block");
+  GemmSmem<BMC>& sm = *reinterpret_cast<GemmSmem<BMC>*>(smem);
+  if (a.vec_scales) {
+    if (tier == HMOE_TIER_NF3) gemm_tile<BMC, W13, kPfNf3, true>(a, tier, r0, loc, tile, sm);
+    else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BMC, W13, kPfNvfp4, true>(a, tier, r0, loc, tile, sm);
+    else gemm_tile<BMC, W13, kPfMxfp4, true>(a, tier, r0, loc, tile, sm);
+  } else {
+    if (tier == HMOE_TIER_NF3) gemm_tile<BMC, W13, kPfNf3, false>(a, tier, r0, loc, tile, sm);
+    else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BMC, W13, kPfNvfp4, false>(a, tier, r0, loc, tile, sm);
+    else gemm_tile<BMC, W13, kPfMxfp4, false>(a, tier, r0, loc, tile, sm);
+  }
+}
+
+// Grid blocks cover the align stage's BMAX-row blocks. An expert's last block holds its
+// remaining slots followed by sentinel padding, so the block runs the smallest tile
+// class (16, 32, 64 or BMAX rows) that reaches its first sentinel: padding rows past
+// that class are neither multiplied nor written, by this launch or the W2 launch (the
+// same slots give it the same class).
+template <int BMAX, bool W13>
 __global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs a) {
   // A 1-D grid. The dispatcher hands consecutive block ids to the eight XCDs in
   // turn (id L runs on XCD L % 8), so id L is given a group of kXcdGroup expert blocks
@@ -541,19 +566,27 @@ __global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs
   const int b = tier ? by - a.nblk0 : by;
   // npad and the block table come from the align stage; clamp to this launch's grid
   // and the tier's expert count so stale scratch cannot index out of range
-  if (b * BM >= a.npad[tier][0] || b >= (tier ? a.nblk1 : a.nblk0)) return;
+  if (b * BMAX >= a.npad[tier][0] || b >= (tier ? a.nblk1 : a.nblk0)) return;
   const int loc = a.bexp[tier][b];
   if ((unsigned)loc >= (unsigned)(tier ? a.E3 : a.E4)) return;
-  __shared__ GemmSmem<BM> sm;
-  if (a.vec_scales) {
-    if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3, true>(a, tier, b, loc, tile, sm);
-    else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4, true>(a, tier, b, loc, tile, sm);
-    else gemm_tile<BM, W13, kPfMxfp4, true>(a, tier, b, loc, tile, sm);
-  } else {
-    if (tier == HMOE_TIER_NF3) gemm_tile<BM, W13, kPfNf3, false>(a, tier, b, loc, tile, sm);
-    else if (a.kept_fmt == HMOE_KEPT_NVFP4) gemm_tile<BM, W13, kPfNvfp4, false>(a, tier, b, loc, tile, sm);
-    else gemm_tile<BM, W13, kPfMxfp4, false>(a, tier, b, loc, tile, sm);
+  const int r0 = b * BMAX;
+  // real rows r of this block: slots [r0, r0 + r) are real, the rest sentinels (>= nslot)
+  const int32_t* sl = a.slots[tier] + r0;
+  int cls = BMAX;
+  if constexpr (BMAX >= 128) if (sl[64] >= a.nslot) cls = 64;
+  if constexpr (BMAX >= 64) if (sl[32] >= a.nslot) cls = 32;
+  if constexpr (BMAX >= 32) if (sl[16] >= a.nslot) cls = 16;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(GemmSmem<BMAX>)];
+  if constexpr (BMAX >= 32) {
+    if (cls == 16) return gemm_tile_any<16, BMAX, W13>(a, tier, r0, loc, tile, smem);
   }
+  if constexpr (BMAX >= 64) {
+    if (cls == 32) return gemm_tile_any<32, BMAX, W13>(a, tier, r0, loc, tile, smem);
+  }
+  if constexpr (BMAX >= 128) {
+    if (cls == 64) return gemm_tile_any<64, BMAX, W13>(a, tier, r0, loc, tile, smem);
+  }
+  gemm_tile_any<BMAX, BMAX, W13>(a, tier, r0, loc, tile, smem);
 }
 
 // x16[t] = fp16(x[t] * 2^-e[t]), e[t] putting the token's largest |x| in [2^14, 2^15);
