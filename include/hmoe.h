@@ -82,7 +82,8 @@ enum { HMOE_STAGE_ROUTE = 0, HMOE_STAGE_W13 = 1, HMOE_STAGE_W2 = 2, HMOE_STAGE_C
  *                every expert is in the kept tier, as NVFP4
  *   block_m      prefill rows per expert block for moe_align: 16, 32, 64 or 128; 0 lets
  *                the library pick from t = max_tokens * top_k / E: 16 below t = 4, 32
- *                below 24, 64 below 64, else 128 */
+ *                below 24, else 128. The prefill GEMM runs a block whose real slots
+ *                fit in 16, 32 or 64 rows as a tile of that many rows. */
 typedef struct hmoe_layer_desc {
     int32_t num_experts;
     int32_t hidden;

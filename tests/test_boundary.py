@@ -77,8 +77,8 @@ def test_query_and_tiers():
     assert q2["kept_format"] == hm.KEPT_NVFP4 and q2["num_nf3"] == 0 and q2["block_m"] == 16
 
 
-@pytest.mark.parametrize("max_tokens,expect", [(1, 16), (127, 16), (128, 32), (767, 32), (768, 64),
-                                               (2047, 64), (2048, 128), (4096, 128)])
+@pytest.mark.parametrize("max_tokens,expect", [(1, 16), (127, 16), (128, 32), (767, 32), (768, 128),
+                                               (2048, 128), (4096, 128)])
 def test_default_block_m(max_tokens, expect):
     # block_m 0: chosen from t = max_tokens * k / E (here E = 256, k = 8: t = max_tokens / 32)
     layer = hm.moe_layer_create(256, 256, 128, 8, max_tokens, hm.KEPT_NVFP4, None, 0)

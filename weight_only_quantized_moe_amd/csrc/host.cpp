@@ -123,14 +123,15 @@ hmoe_status check_weights(const hmoe::Layer& L, const hmoe_weights* w) {
 extern "C" {
 
 // Prefill rows per expert block when the caller leaves it to the library: from the mean
-// number of slots per expert at max_tokens, t = max_tokens * k / E. Measured on the
-// GLM-class layer (skewed routing) on MI355X: 16 rows are fastest below t = 4, 32 up to
-// t = 24, 64 up to t = 64 and 128 above (padding waste against per-block weight cost).
+// number of slots per expert at max_tokens, t = max_tokens * k / E. The GEMM runs an
+// expert's last, partly padded block as a 16-, 32- or 64-row tile, so a large block_m
+// costs little for small experts; but its LDS stage allows two blocks per CU where a
+// 32-row block_m allows three. Measured on the GLM-class layer on MI355X, skewed and
+// unskewed routing: 16 rows are fastest below t = 4, 32 below t = 24 and 128 above.
 static int auto_block_m(long max_tokens, long k, long E) {
   const long t = max_tokens * k;
   if (t < 4 * E) return 16;
   if (t < 24 * E) return 32;
-  if (t < 64 * E) return 64;
   return 128;
 }
 
