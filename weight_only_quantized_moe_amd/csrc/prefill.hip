@@ -54,10 +54,15 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// LDS tiles hold rows of 64 16-bit values (eight 16-byte chunks) with chunk c of row
-// r stored at chunk c ^ (r & 7): the 16-byte MFMA operand reads of 16 consecutive
-// rows then spread over all banks.
-__device__ __forceinline__ int swz(int r, int c) { return 8 * (c ^ (r & 7)); }
+// LDS tiles hold rows of 64 16-bit values (eight 16-byte chunks, one row spanning all
+// 32 four-byte banks) with chunk c of row r stored at chunk c ^ (r & 7) ^ (2 * bit 4
+// of r). The low term spreads the 16-byte MFMA operand reads of 16 consecutive rows
+// over all banks (a 16-byte access is served eight lanes at a time); the high term
+// separates rows r and r + 16, which the decoding threads of one eight-lane group
+// write in the same step (without it those stores conflict two ways).
+__device__ __forceinline__ int swz_lo(int r) { return r & 7; }
+__device__ __forceinline__ int swz_hi(int r) { return (r >> 3) & 2; }
+__device__ __forceinline__ int swz(int r, int c) { return 8 * (c ^ swz_lo(r) ^ swz_hi(r)); }
 
 struct PrefillArgs {
   const uint8_t* kq;
@@ -390,14 +395,19 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int r0
   auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
-      const int kk = swz(lane, 4 * ks + g);  // row bases are multiples of 16
+      // row bases are multiples of 16: the low swizzle term comes from j, the high
+      // one from the base
+      const int kk = 8 * ((4 * ks + g) ^ swz_lo(j));
       uint4 bq[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        bq[nt] = *reinterpret_cast<const uint4*>(&Bs[buf][tile_row<BM, W13>(wn, nt) + j][kk]);
+      for (int nt = 0; nt < NT; ++nt) {
+        const int tr = tile_row<BM, W13>(wn, nt);
+        bq[nt] = *reinterpret_cast<const uint4*>(&Bs[buf][tr + j][kk ^ (8 * swz_hi(tr))]);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint4 aq = *reinterpret_cast<const uint4*>(&As[buf][(wm * MT + mt) * 16 + j][kk]);
+        const int ar = (wm * MT + mt) * 16;
+        const uint4 aq = *reinterpret_cast<const uint4*>(&As[buf][ar + j][kk ^ (8 * swz_hi(ar))]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
