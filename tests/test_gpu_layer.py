@@ -42,6 +42,33 @@ def test_tiny_layer(hm, fmt, bitmap, M, block_m):
     check_output(y, ref["y"], f"tiny {fmt} {bitmap} M={M} bm={block_m}")
 
 
+# Expert slot counts on both sides of every prefill tile-class boundary (the GEMM
+# runs an align block's real slots as a 16-, 32-, 64- or block_m-row tile), in both
+# tiers: token t takes experts order[t] and order[t + M] of the sorted slot list, so
+# each expert ends up with exactly its count.
+@pytest.mark.parametrize("fmt,counts", [
+    ("nvfp4", [16, 17, 32, 33, 64, 65, 128, 129]),
+    ("mxfp4", [129, 128, 65, 64, 33, 32, 17, 16])])
+@pytest.mark.parametrize("block_m", [64, 128])
+def test_prefill_tile_class_boundaries(hm, fmt, counts, block_m):
+    packed, w = tiny_packed(fmt, "prefix")
+    slots = np.repeat(np.arange(8), counts)
+    M = slots.size // 2
+    assert slots.size == 2 * M and max(counts) < M
+    rng = np.random.default_rng([11, block_m])
+    lg = (rng.standard_normal((M, 8)) * 0.1 - 2.0).astype(np.float32)
+    t = np.arange(M)
+    lg[t, slots[:M]] = (3.0 + rng.standard_normal(M) * 0.1).astype(np.float32)
+    lg[t, slots[M:]] = (2.0 + rng.standard_normal(M) * 0.1).astype(np.float32)
+    ids, _ = OL.route(lg, 2)
+    assert np.array_equal(np.bincount(np.asarray(ids).ravel(), minlength=8), counts)
+    layer = make_layer(packed, 256, block_m)
+    wts = hm.DeviceWeights(packed)
+    x = synth.activations_bf16(w, M)
+    y, _ = run_forward(layer, wts, x, lg)
+    check_output(y, OL.forward(packed, x, lg)["y"], f"tile classes {fmt} bm={block_m}")
+
+
 def test_tiny_layer_wider_topk_and_experts(hm):
     packed, w = tiny_packed("nvfp4", "prefix", E=16, H=384, I=256, k=4, seed=3)
     # experts 0-3 kept; make the map irregular
