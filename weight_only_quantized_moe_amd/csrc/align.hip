@@ -13,6 +13,10 @@ namespace hmoe {
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
+// s_waitcnt operand waiting for LDS only (gfx9 fields: vmcnt 63, expcnt 7, lgkmcnt 0):
+// the placement loop orders its position reads and counter updates in LDS but leaves
+// its global stores of slot ids in flight
+constexpr int kWaitLdsOnly = 0xC07F;
 
 struct AlignArgs {
   const int32_t* ids;
@@ -126,13 +130,13 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
     int pos = 0;
     if (valid) pos = s_w[wave][e] + rank;
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
     if (valid) {
       a.slots[s_tc[e] >> 16][pos] = s;
       if (rank == cnt - 1) s_w[wave][e] += cnt;
     }
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
   }
 }
 
