@@ -23,9 +23,12 @@
 //       factor, both exact. The per-tensor fp32 scale returns in the epilogue.
 //   MXFP4: e2m1 * 2^(b - bref) with bref the row's largest E8M0 byte (exact unless a
 //       block is 2^24 below the row's largest); 2^(bref - 127) returns in the epilogue.
-//   NF3: the 64-entry table holds scaled level pairs (kNF3TableScaleF16); each K step
-//       is one group, so its two MFMAs accumulate into a fresh fp32 partial that is
-//       multiplied by the group's fp16 scale before it joins the accumulator.
+//   NF3: the 64-entry table holds level pairs times kNF3TableScaleF16 in fp16 (within
+//       3.5e-5 relative of the exact products); a unit's pairs are multiplied (packed
+//       fp16) by its group scale times 2^(15 - ref), ref the largest fp16 exponent
+//       field among the row's group scales, so each weight takes one fp16 rounding of
+//       level times scale; 2^(ref - 15) and 1 / kNF3TableScaleF16 return in the
+//       epilogue.
 #include <type_traits>
 #include <utility>
 
