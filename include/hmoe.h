@@ -257,8 +257,11 @@ hmoe_status hybrid_moe_forward_stage(const hmoe_layer* layer, const hmoe_weights
                                      int32_t stage, hipStream_t stream);
 
 /* Test hook: dequantises one whole expert tensor (W13: [2I, H] or W2: [H, I]) of global
- * expert `expert` with the same device decode routines the forward kernels use, and
- * writes the canonical values: out_f32 fp32 [rows, K] and/or out_bf16 bf16 bits
+ * expert `expert` and writes the canonical values. It shares the format primitives of
+ * the forward kernels (the hardware E2M1 and E4M3 conversions, the E8M0 scale, the NF3
+ * level constants) but not their decode paths, which fold block scales into 16-bit
+ * operands, scaled level tables or fp32 partials and are checked through the layer
+ * output. Writes: out_f32 fp32 [rows, K] and/or out_bf16 bf16 bits
  * [rows, K] (either may be NULL). Canonical values: NVFP4 fp32(e2m1 * e4m3) * g (one
  * rounding), MXFP4 e2m1 * 2^(b - 127) (exact), NF3 level[q] * fp16 scale (one
  * rounding); the bf16 form is the fp32 value rounded to nearest even.

@@ -155,13 +155,15 @@ def expert_mlp(x: np.ndarray, w13: np.ndarray, w2: np.ndarray):
     return h, h @ w2.astype(np.float64).T
 
 
-def forward(layer: dict, x_bits: np.ndarray, logits: np.ndarray, tokens=None):
+def forward(layer: dict, x_bits: np.ndarray, logits: np.ndarray, tokens=None, threads: int = 1):
     """The layer: route once, run every selected (token, expert) pair through
     the expert's MLP in its own tier, and add the outputs into one top-k
     weighted sum y[t] = sum_j w[t, j] * o[t, j]. `tokens` restricts the
     returned rows to a subset (the routing result is still for every token).
-    Returns ids, weights, per-slot h (only for the computed tokens) and y
-    (fp64, one row per computed token)."""
+    `threads` > 1 dequantises and runs several experts at once; the outputs are
+    still added into y one expert at a time in ascending expert id, so the result
+    does not depend on it. Returns ids, weights, per-slot h (only for the computed
+    tokens) and y (fp64, one row per computed token)."""
     E, k = layer["E"], layer["top_k"]
     ids, w = route(logits, k)
     M = ids.shape[0]
@@ -171,13 +173,28 @@ def forward(layer: dict, x_bits: np.ndarray, logits: np.ndarray, tokens=None):
     y = np.zeros((len(tokens), H), dtype=np.float64)
     h_all = {}
     sel = ids[tokens]
-    for e in sorted(set(int(v) for v in sel.reshape(-1))):
+    experts = sorted(set(int(v) for v in sel.reshape(-1)))
+
+    def run(e):
         rows, cols = np.nonzero(sel == e)
         w13, w2 = expert_weights(layer, e)
         h, o = expert_mlp(x[rows], w13, w2)
+        return rows, cols, h, o
+
+    def add(result):
+        rows, cols, h, o = result
         y[rows] += w[np.asarray(tokens)[rows], cols][:, None] * o
         for r, c, hh in zip(rows, cols, h):
             h_all[int(tokens[r]) * k + int(c)] = hh
+
+    if threads > 1 and len(experts) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            for result in ex.map(run, experts):   # results come back in submission order
+                add(result)
+    else:
+        for e in experts:
+            add(run(e))
     return {"ids": ids, "w": w, "h": h_all, "y": y, "tokens": tokens}
 
 

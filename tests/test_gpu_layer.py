@@ -84,7 +84,7 @@ def test_tiny_layer_wider_topk_and_experts(hm):
 @pytest.mark.parametrize("kept,bit_map", [("nvfp4", "prefix"), ("mxfp4", "prefix"),
                                            ("nvfp4", None)])
 def test_decode_shared_experts(hm, kept, bit_map):
-    """Decode with K a multiple of 512 (the matrix-core W13 path) in every kept format:
+    """Decode with K a multiple of 512 in every kept format:
     ordinary routing at M = 1, 3, 8, and routing forced onto the same four experts for
     every token (each expert then serves all M = 8 tokens at once)."""
     packed, w = tiny_packed(kept, bit_map, E=16, H=512, I=256, k=4, seed=5)
@@ -185,33 +185,186 @@ def test_hip_graph_replay(hm, qwen):
 
 # ---------------------------------------------------------------- GLM-class, full size
 
-def _glm_case(hm, workload, tokens):
+ORACLE_THREADS = 16
+
+
+def probe_tokens(ids: np.ndarray, tier: np.ndarray, block_m: int, n_total: int, seed: int):
+    """Tokens whose slots reach every part of the prefill grid: for each tier and each
+    tile class (16, 32, 64 or block_m rows) that some expert's last align block runs,
+    up to three such experts with the first and the last real slot of that block; the
+    hottest expert of each tier (its last block and a full one); up to four experts of
+    each tier holding 1-16 slots; then random tokens up to n_total."""
+    M, k = ids.shape
+    flat = ids.reshape(-1)
+    order = np.argsort(flat, kind="stable")            # slots grouped by expert, ascending
+    counts = np.bincount(flat, minlength=tier.size)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    classes = [c for c in (16, 32, 64) if c < block_m] + [block_m]
+    picked = set()
+
+    def slot_token(e, j):                                # token of expert e's j-th slot
+        picked.add(int(order[starts[e] + j]) // k)
+
+    for t in (0, 1):
+        members = [e for e in range(tier.size) if tier[e] == t and counts[e] > 0]
+        if not members:
+            continue
+        by_class = {c: [] for c in classes}
+        for e in members:
+            c = int(counts[e])
+            last0 = (c - 1) // block_m * block_m            # first slot of the last block
+            real = c - last0
+            by_class[next(x for x in classes if x >= real)].append((e, last0, c))
+        for c in classes:
+            for e, last0, cnt in by_class[c][:3]:
+                slot_token(e, last0)
+                slot_token(e, cnt - 1)
+        hot = max(members, key=lambda e: counts[e])
+        slot_token(hot, int(counts[hot]) - 1)
+        slot_token(hot, min(block_m, int(counts[hot])) - 1)
+        for e in [e for e in members if counts[e] <= 16][:4]:
+            slot_token(e, 0)
+            slot_token(e, int(counts[e]) - 1)
+    rng = np.random.default_rng(seed)
+    rest = [t for t in rng.permutation(M).tolist() if t not in picked]
+    picked.update(rest[:max(0, n_total - len(picked))])
+    return sorted(picked)
+
+
+def _glm_case(hm, workload, tokens=None, n_probe=None):
+    """The layer at full size with the block_m the library picks for w.M; the oracle
+    computes `tokens` (all of them when None), or, with n_probe, the tokens of
+    probe_tokens."""
     w = workload
     packed = synth.packed_layer(w)
     wts = hm.DeviceWeights(packed)
-    layer = make_layer(packed, w.M, 32)
+    layer = make_layer(packed, w.M)
     x = synth.activations_bf16(w, w.M)
     lg = synth.router_logits(w, w.M)
     y, scratch = run_forward(layer, wts, x, lg)
-    ref = OL.forward(packed, x, lg, tokens=tokens)
-    check_output(y[tokens], ref["y"], w.name)
+    if n_probe is not None:
+        ids, _ = OL.route(lg, w.top_k)
+        tier, _ = OL.tier_map(packed["bit_map"], w.E)
+        tokens = probe_tokens(ids, tier, hm.moe_layer_query(layer)["block_m"], n_probe, w.M)
+    ref = OL.forward(packed, x, lg, tokens=tokens, threads=ORACLE_THREADS)
+    rows = ref["tokens"]
+    check_output(y[rows], ref["y"], f"{w.name} ({len(rows)} tokens)")
     tids, _ = hm.moe_topk_view(layer, scratch, w.M)
     assert np.array_equal(tids.cpu().numpy(), ref["ids"]), f"{w.name}: top-k ids"
     del wts
     torch_mod().cuda.empty_cache()
+    return rows
 
 
 def test_glm_decode_m8(hm):
-    _glm_case(hm, synth.glm_decode(8), [0, 5])
+    _glm_case(hm, synth.glm_decode(8))
 
 
-def test_glm_prefill_m4096_sampled(hm):
-    _glm_case(hm, synth.glm_prefill(4096), [0, 1234, 4095])
+def test_glm_prefill_m4096_probed(hm):
+    rows = _glm_case(hm, synth.glm_prefill(4096), n_probe=64)
+    assert len(rows) >= 64
 
 
-def test_glm_mxfp4_m512_and_uniform_control(hm):
-    _glm_case(hm, synth.glm_mxfp4(512), [0, 511])
-    _glm_case(hm, synth.glm_uniform(512), [7])
+def test_glm_mxfp4_m512_probed(hm):
+    _glm_case(hm, synth.glm_mxfp4(512), n_probe=64)
+
+
+def test_glm_uniform_control_m512(hm):
+    _glm_case(hm, synth.glm_uniform(512))
+
+
+# ---------------------------------------------------------------- K a multiple of 512
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("block_m", [64, 128])
+def test_prefill_tile_classes_vector_scales(hm, fmt, block_m):
+    """Tile-class boundaries with H and I multiples of 512, so both GEMMs take their
+    scales as 16-byte vectors of eight K steps: 16 experts (8 kept, 8 NF3), top-4, the
+    slot counts set on both sides of every class boundary in both tiers; every output
+    checked."""
+    counts = [16, 17, 32, 33, 64, 65, 128, 129, 129, 128, 65, 64, 33, 32, 17, 20]
+    E, k = 16, 4
+    w = synth.Workload("vs", E, 1024, 512, k, 256, fmt, 8, "prefix", seed=7)
+    packed = OL.quantize_layer(w.E, w.H, w.I, k, synth.bit_map(w), fmt,
+                               lambda e: synth.master_weights(w, e))
+    slots = np.repeat(np.arange(E), counts)
+    M = slots.size // k
+    assert slots.size == k * M and max(counts) <= M
+    rng = np.random.default_rng([13, block_m])
+    lg = (rng.standard_normal((M, E)) * 0.1 - 4.0).astype(np.float32)
+    t = np.arange(M)
+    for r in range(k):
+        lg[t, slots[r * M:(r + 1) * M]] = (3.0 - r + rng.standard_normal(M) * 0.05).astype(np.float32)
+    ids, _ = OL.route(lg, k)
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=E), counts)
+    layer = make_layer(packed, M, block_m)
+    wts = hm.DeviceWeights(packed)
+    x = synth.activations_bf16(w, M)
+    y, _ = run_forward(layer, wts, x, lg)
+    check_output(y, OL.forward(packed, x, lg)["y"], f"vector scales {fmt} bm={block_m}")
+
+
+# ---------------------------------------------------------------- activation range, scale signs
+
+def _large_x(w, M, seed):
+    """N(0, 1) tokens times 2^7 with three channels per token at +-2^12 (bf16 bits)."""
+    rng = np.random.default_rng([seed, M])
+    x = rng.standard_normal((M, w.H)).astype(np.float32) * np.float32(2.0 ** 7)
+    ch = rng.integers(0, w.H, (M, 3))
+    x[np.arange(M)[:, None], ch] = np.where(rng.random((M, 3)) < 0.5, -1.0, 1.0) * 2.0 ** 12
+    return F.bf16_bits(x)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_large_activations(hm, fmt):
+    """Tokens whose SwiGLU output exceeds the fp16 range (the oracle's |h| > 65504), through
+    decode (M = 8) and prefill (M = 64, block_m 16 and 64)."""
+    packed, w = tiny_packed(fmt, "prefix")
+    wts = hm.DeviceWeights(packed)
+    for M, block_m in ((8, 16), (64, 16), (64, 64)):
+        x = _large_x(w, M, 5)
+        lg = synth.router_logits(w, M)
+        ref = OL.forward(packed, x, lg)
+        assert max(np.abs(h).max() for h in ref["h"].values()) > 65504.0
+        layer = make_layer(packed, M, block_m)
+        y, _ = run_forward(layer, wts, x, lg)
+        check_output(y, ref["y"], f"large x {fmt} M={M} bm={block_m}")
+
+
+def _signed_scale_layer(seed):
+    """4 experts (0, 1 NVFP4; 2, 3 NF3), H = 512, I = 256, top-2, random codes, block
+    scales of either sign: E4M3 bytes 0x70-0x7E with a random sign bit and per-tensor
+    scales near 3e-5 (the magnitudes the NVFP4 quantiser gives N(0, 0.02) weights), NF3
+    fp16 scales of +-U(0.035, 0.065)."""
+    E, H, I, k = 4, 512, 256, 2
+    bm = np.array([4, 4, 3, 3], np.uint8)
+    lay = synth.empty_packed_layer(E, H, I, k, "nvfp4", bm)
+    r = np.random.default_rng(seed)
+    for d in (lay["kept"], lay["nf3"]):
+        for key in ("w13_q", "w2_q"):
+            d[key][:] = r.integers(0, 256, d[key].shape, dtype=np.uint8)
+    for key in ("w13_s", "w2_s"):
+        a = lay["kept"][key]
+        a[:] = (r.integers(0x70, 0x7F, a.shape) | (r.integers(0, 2, a.shape) << 7)).astype(np.uint8)
+        a = lay["nf3"][key]
+        v = r.uniform(0.035, 0.065, a.shape) * np.where(r.random(a.shape) < 0.5, -1.0, 1.0)
+        a[:] = v.astype(np.float16).view(np.uint16)
+    for key in ("w13_g", "w2_g"):
+        lay["kept"][key][:] = r.uniform(2.5e-5, 3.5e-5, E // 2).astype(np.float32)
+    return lay
+
+
+def test_signed_block_scales_forward(hm):
+    """Negative E4M3 and fp16 block scales through the decode and prefill forwards."""
+    packed = _signed_scale_layer(21)
+    w = synth.Workload("signed", 4, 512, 256, 2, 64, "nvfp4", 2, "prefix", seed=21)
+    wts = hm.DeviceWeights(packed)
+    for M, block_m in ((8, 16), (64, 16), (64, 64)):
+        x = synth.activations_bf16(w, M)
+        lg = synth.router_logits(w, M)
+        layer = make_layer(packed, M, block_m)
+        y, _ = run_forward(layer, wts, x, lg)
+        check_output(y, OL.forward(packed, x, lg)["y"], f"signed scales M={M} bm={block_m}")
 
 
 # ---------------------------------------------------------------- maximum sizes, empty tier

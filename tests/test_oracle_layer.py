@@ -154,6 +154,21 @@ def test_layer_brute_force_loops():
         assert np.allclose(out["y"][t], y, rtol=1e-10, atol=1e-13)
 
 
+def test_forward_threads_do_not_change_the_result():
+    """Running experts on a thread pool adds their outputs in the same ascending
+    expert order: bit-identical y and h, for all tokens and for a token subset."""
+    bm = np.array([4, 3, 4, 3, 4, 3, 3, 3], np.uint8)
+    lay, w = _tiny_layer(bm)
+    x = synth.activations_bf16(w, 12)
+    lg = synth.router_logits(w, 12)
+    for tokens in (None, [0, 5, 11]):
+        a = L.forward(lay, x, lg, tokens=tokens)
+        b = L.forward(lay, x, lg, tokens=tokens, threads=4)
+        assert np.array_equal(a["y"], b["y"])
+        assert a["h"].keys() == b["h"].keys()
+        assert all(np.array_equal(a["h"][s], b["h"][s]) for s in a["h"])
+
+
 def test_tier_additivity():
     bm = np.array([4, 3, 4, 3, 4, 3, 3, 3], np.uint8)
     lay, w = _tiny_layer(bm)

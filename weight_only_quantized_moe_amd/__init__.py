@@ -277,6 +277,10 @@ def moe_repack(layer: Layer, experts, dst: "DeviceWeights", stream=None) -> None
     tensors in the checkpoint layout (kept tier: w13_q, w13_s, w13_g, w2_q, w2_s, w2_g;
     NF3 tier: w13_lo, w13_hi, w13_s, w2_lo, w2_hi, w2_s), written into the tier-local
     arrays of `dst`."""
+    info = moe_layer_query(layer)
+    if len(experts) != info["num_experts"]:
+        raise ValueError(f"moe_repack: {len(experts)} experts given, the layer has "
+                         f"{info['num_experts']}")
     arr = (ExpertSrc * len(experts))()
     for i, ex in enumerate(experts):
         nf3 = "w13_lo" in ex

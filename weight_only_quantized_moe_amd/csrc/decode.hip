@@ -7,8 +7,8 @@
 //
 // Work split: every (token, top-k) slot is one pass over its expert's rows (W13:
 // pairs of a gate row i and its up row I + i; W2: rows n). The routing kernel lists
-// the passes grouped by expert, so a token pair sharing an expert streams the same
-// rows back to back (the second time from cache). Passes are cut into chunks of
+// the passes in slot order (token-major); two tokens that share an expert stream its
+// rows in separate passes, the later one mostly from cache. Passes are cut into chunks of
 // P * RI rows (or pairs); the M * k * chunks-per-pass units form one flat range and
 // every wave of a persistent grid takes an equal contiguous run of it, so the work
 // is balanced whatever the expert multiplicities are, and a wave's first load (its

@@ -1,5 +1,9 @@
 // Dequantisation test hook: writes one expert tensor's canonical fp32 values (and
-// their bf16 rounding) with the device decode primitives the forward kernels use.
+// their bf16 rounding). It shares the format primitives of device_common.h with the
+// forward kernels (the hardware E2M1 / E4M3 conversions, the E8M0 scale and the NF3
+// level bit patterns) but not their decode paths: the forward kernels fold scales
+// into 16-bit operands, scaled level tables and fp32 partials, which only the layer
+// output tolerance covers.
 // Canonical values: NVFP4 fp32(e2m1 * e4m3) * g (the first product is exact, the
 // per-tensor multiply is the one rounding), MXFP4 e2m1 * 2^(b - 127) (exact), NF3
 // level[q] * fp16 scale (one rounding).

@@ -17,7 +17,11 @@
 //   x:  bf16 tokens are converted once per token to fp16 times 2^-e, e chosen so the
 //       token's largest |x| lands in [2^14, 2^15) (exact for every element within 2^29
 //       of it); 2^e returns in the W13 epilogue.
-//   h:  W13's SwiGLU output is stored as fp16, saturated at +-65504.
+//   h:  W13's SwiGLU output is stored as fp16 times 2^-he, he = 2 (e + 14) with e
+//       the token's x exponent above (clamped to [-100, 100]): gate and up grow
+//       with the token's largest |x|, so h / max|x|^2 stays within the product of
+//       the gate and up rows' L1 norms whatever the activations' scale. The stored
+//       value saturates at +-65504 only beyond that; 2^he returns in the W2 epilogue.
 //   NVFP4: e2m1 * E4M3 has at most 6 significant bits and lies in [2^-10, 2688]: the
 //       conversion applies the scale's power of two, a packed fp16 multiply its 1.m
 //       factor, both exact. The per-tensor fp32 scale returns in the epilogue.
@@ -77,7 +81,7 @@ struct PrefillArgs {
   int rows_w;  // rows of the weight tensor per expert
   int K;
   const uint16_t* act;   // W13: x fp16 [M, H] (scaled per token); W2: h fp16 [cap0 + cap1, I]
-  const int32_t* xe;     // W13: per-token exponent of the x scaling
+  const int32_t* xe;     // per-token exponent of the x scaling (W2: gives h's scaling)
   int k, nslot;
   const int32_t* slots[2];
   const int32_t* bexp[2];
@@ -95,6 +99,9 @@ struct PrefillArgs {
 };
 
 enum : int { kPfNvfp4 = 0, kPfMxfp4 = 1, kPfNf3 = 2 };
+
+// exponent he of a token's h scaling from its x exponent e (see the header)
+__device__ __forceinline__ int h_exponent(int e) { return min(max(2 * (e + 14), -100), 100); }
 
 __device__ __forceinline__ uint32_t mul_f16x2(uint32_t v, f16x2 m) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) * m);
@@ -138,7 +145,9 @@ struct GemmSmem {
 __device__ __forceinline__ void nvfp4_block_f16(uint32_t q0, uint32_t q1, uint32_t sbyte,
                                                 uint32_t* w) {
   const float s = __builtin_amdgcn_cvt_f32_fp8(sbyte, 0);
-  const float mu32 = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  // +-1.m of the scale: the conversion applies the scale's exponent only, so its sign
+  // rides on this factor
+  const float mu32 = __uint_as_float((__float_as_uint(s) & 0x807FFFFFu) | 0x3F800000u);
   const _Float16 mu = (s == 0.0f) ? (_Float16)0.0f : (s != s ? (_Float16)s : (_Float16)mu32);
   const f16x2 m = {mu, mu};
   w[0] = mul_f16x2(e2m1x2_f16<0>(q0, s), m);
@@ -522,15 +531,19 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int r0
         const int m = (wm * MT + mt) * 16 + 4 * g + q;
         const int slot = bslots[m];
         if (W13) {
-          // x was scaled by 2^-xe[token]
-          const float xs = (unsigned)slot < (unsigned)a.nslot ? __builtin_ldexpf(1.0f, a.xe[slot / a.k]) : 0.0f;
+          // x was scaled by 2^-e, h is stored times 2^-he
+          const bool real = (unsigned)slot < (unsigned)a.nslot;
+          const int e = real ? a.xe[slot / a.k] : 0;
+          const float xs = real ? __builtin_ldexpf(1.0f, e) : 0.0f;
           const float gate = acc[mt][nt][q] * gf * xs;
           const float up = acc[mt][nt + NT / 2][q] * uf * xs;
-          const float h = fminf(fmaxf(silu(gate) * up, -65504.0f), 65504.0f);
+          const float hv = __builtin_ldexpf(silu(gate) * up, -h_exponent(e));
+          const float h = fminf(fmaxf(hv, -65504.0f), 65504.0f);
           a.h_out[(hbase + m) * a.I + n] = (uint16_t)(pack_f16(h, 0.0f) & 0xFFFFu);
         } else {
           if ((unsigned)slot < (unsigned)a.nslot)
-            a.o_out[(size_t)slot * a.H + n] = acc[mt][nt][q] * gf * a.topk_w[slot];
+            a.o_out[(size_t)slot * a.H + n] =
+                __builtin_ldexpf(acc[mt][nt][q] * gf * a.topk_w[slot], h_exponent(a.xe[slot / a.k]));
         }
       }
     }
@@ -744,6 +757,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     c.rows_w = L.H;
     c.K = L.I;
     c.act = h;
+    c.xe = xe;
     c.o_out = o;
     c.topk_w = w;
     c.ntile = L.H / kBN;
