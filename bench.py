@@ -4,11 +4,14 @@ one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Default workload: the Qwen3-MoE-shaped decode layer (E=128, H=2048, I=768, top-8,
-32 NVFP4 + 96 NF3 experts), M = 8 tokens per step, with the M = 1, 2, 4 points of
-the decode sweep reported beside it. Other workloads (--workload): glm_decode
-(E=256, H=6144, I=2048, M=8), glm_prefill (M=4096, skewed routing), glm_mxfp4
-(MXFP4 kept tier, M=512) and glm_uniform (no bit map, uniform NVFP4, M=512).
+Default run: both halves of the metric.
+  * decode: the Qwen3-MoE-shaped layer (E=128, H=2048, I=768, top-8, 32 NVFP4 + 96
+    NF3 experts) at M = 8 tokens per step -- `value` is its tokens/s -- with the
+    M = 1, 2, 4 points of the decode sweep beside it;
+  * prefill: the GLM-class layer (E=256, H=6144, I=2048, top-8, 64 NVFP4 + 192 NF3,
+    skewed routing) at M = 4096, reported under "prefill" with its TFLOP/s.
+--workload NAME runs one workload alone: qwen_decode, glm_decode (M=8), glm_prefill
+(M=4096), glm_mxfp4 (MXFP4 kept tier, M=512) or glm_uniform (no bit map, M=512).
 
 One step is one hybrid_moe_forward over one batch: routing, grouping or align,
 both tiers' W13 + SwiGLU, W2 + weighted combine. Steps replay HIP graphs of the
@@ -16,10 +19,14 @@ forward that rotate over enough copies of the packed weights to exceed the
 256 MB Infinity Cache, so every step reads its experts from HBM. Inputs are
 synthetic (seeded), resident in HBM before timing starts.
 
-Prints one JSON line. `roofline` covers the dominant kernel (decode: the W13
-GEMV; prefill: the W13 grouped GEMM), timed live with HIP events on the launch
-stream; `cpu_baseline` times the CPU oracle on a bounded sample of the same
-workload.
+Each workload carries a `roofline` of its dominant kernel (decode: the W13 GEMV;
+prefill: the W13 grouped GEMM), bound by HBM or by the MFMA units as the layer's
+arithmetic intensity says. Its `achieved`/`frac` use the kernel's average duration
+from the committed rocprofv3 kernel trace (profiles/kernel_times.json) when that was
+taken on the current kernel sources, and otherwise the live HIP-event timing of
+back-to-back launches on the launch stream, which is always reported beside it.
+`cpu_baseline` times the CPU oracle (median of 5 runs for decode, 3 for prefill) on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -38,6 +45,7 @@ METRIC = "MoE-layer decode tok/s + HBM GB/s (M<=8); prefill TFLOP/s (M=4096)"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 * 1024 * 1024
+RIDGE_FLOP_PER_BYTE = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
 
 
 def log(msg):
@@ -185,6 +193,7 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
            "w13_launch_us": w13_launch_us,
            "layer_bytes_resident": layer_bytes, "desc": describe(w, packed)}
     io_bytes = M * w.H * 2 + M * w.E * 4 + M * w.H * 2        # x, logits, y
+    flops = 6.0 * M * k * w.H * w.I
     if M <= hm.DECODE_MAX_M:
         v = hm.moe_decode_view(layer, scratch)
         counts = v["counts"].cpu().numpy()
@@ -192,9 +201,10 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
         n_tier = {"kept": nk, "nf3": nd - nk}
         w13 = sum(n_tier[t] * eb[t]["w13"] for t in eb)
         w2 = sum(n_tier[t] * eb[t]["w2"] for t in eb)
-        res.update(distinct_experts=nd, distinct_kept=nk,
+        # W13 GEMV: the touched experts' W13, x read, h written (fp32)
+        res.update(distinct_experts=nd, distinct_kept=nk, touched_experts=n_tier,
                    layer_bytes=w13 + w2 + io_bytes,
-                   w13_bytes=w13 + M * w.H * 2 + M * k * w.I * 2)
+                   w13_bytes=w13 + M * w.H * 2 + M * k * w.I * 4)
     else:
         touched = {}
         for t, name in ((0, "kept"), (1, "nf3")):
@@ -203,8 +213,11 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
             off = hm.moe_align_view(layer, scratch, t)["expert_off"].cpu().numpy()
             touched[name] = int((np.diff(off) > 0).sum())
         wbytes = sum(touched[t] * (eb[t]["w13"] + eb[t]["w2"]) for t in touched)
+        w13w = sum(touched[t] * eb[t]["w13"] for t in touched)
+        # W13 grouped GEMM: the touched experts' W13, the fp16 x read, h written (fp16)
         res.update(touched_experts=touched, layer_bytes=wbytes + io_bytes,
-                   flops=6.0 * M * k * w.H * w.I, w13_flops=4.0 * M * k * w.H * w.I)
+                   w13_bytes=w13w + M * w.H * 2 + M * k * w.I * 2)
+    res.update(flops=flops, w13_flops=4.0 * M * k * w.H * w.I)
     res["packed"] = packed
     res["inputs"] = (synth.activations_bf16(w, w.M), synth.router_logits(w, w.M))
     del graphs, wts, base
@@ -212,33 +225,98 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
     return res
 
 
-def cpu_baseline(packed, x_bits, logits, budget_s=15.0, tokens=None):
-    """The oracle as it stands, on the same layer and batch (or on a sample of its
-    tokens, routed with the whole batch), repeated until about budget_s seconds of
-    CPU work."""
+def rocprof_launch_us(kernel_key, src_hash):
+    """Average duration (us) of a workload's dominant kernel in the committed rocprofv3
+    kernel trace (profiles/kernel_times.json), if it was taken on the current sources."""
+    path = os.path.join(ROOT, "profiles", "kernel_times.json")
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except Exception:
+        return None, None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None, None
+    return float(rec["avg_us"]), rec.get("profile")
+
+
+def roofline(w, r, src, decode):
+    """Roofline of the dominant kernel (the W13 stage). The bound follows the layer's
+    arithmetic intensity (flops per algorithmic byte) against the ridge point of the
+    peaks."""
+    intensity = r["flops"] / r["layer_bytes"]
+    hbm = decode or intensity < RIDGE_FLOP_PER_BYTE
+    key = ("decode_w13_" if decode else "prefill_w13_") + w.name
+    if hbm:
+        work, scale, peak, unit = r["w13_bytes"], 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        work, scale, peak, unit = r["w13_flops"], 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    kernel = ("w13_gemv_kernel (decode W13 + SwiGLU)" if decode
+              else "grouped_gemm_kernel<W13> (prefill W13 + SwiGLU)")
+    ev_us = r["w13_launch_us"]
+    prof_us, prof = rocprof_launch_us(key, src)
+    us = prof_us if prof_us is not None else ev_us
+    achieved = work / (us * 1e-6) / scale
+    rec = {"bound": "hbm" if hbm else "mfma", "kernel": kernel, "achieved": achieved, "peak": peak,
+           "unit": unit, "frac": achieved / peak,
+           "traffic": pmc_traffic(key, src, None),
+           ("algorithmic_bytes" if hbm else "algorithmic_flops"): work,
+           "avg_launch_us": us,
+           "timing": "rocprofv3 kernel trace" if prof_us is not None else "hip events",
+           "profile": prof,
+           "avg_launch_us_hip_events": ev_us,
+           "achieved_hip_events": work / (ev_us * 1e-6) / scale,
+           "frac_hip_events": work / (ev_us * 1e-6) / scale / peak,
+           "intensity_flop_per_byte": intensity}
+    return rec
+
+
+def cpu_baseline(packed, x_bits, logits, runs, tokens=None):
+    """The oracle as it stands on the same layer and batch (or on a sample of its tokens,
+    routed with the whole batch): `runs` forwards, the median reported."""
     from oracle import layer as OL
-    threads = None
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         pass
-    runs = 0
-    t0 = time.perf_counter()
-    while True:
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
         OL.forward(packed, x_bits, logits, tokens=tokens)
-        runs += 1
-        if time.perf_counter() - t0 >= budget_s or runs >= 20:
-            break
-    el = time.perf_counter() - t0
+        times.append(time.perf_counter() - t0)
+    med = sorted(times)[len(times) // 2]
     M = x_bits.shape[0]
     n = M if tokens is None else len(tokens)
-    what = f"the M={M} batch" if tokens is None else f"{n} of the M={M} tokens (routing all {M})"
-    return {"value": n * runs / el, "unit": "tok/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle", "runs": runs, "seconds": el,
-            "sample": f"{runs} oracle forwards of {what}: route, fp32 dequant of the touched "
-                      f"experts, fp64 SwiGLU MLPs, combine; numpy, BLAS threads as `cores`, "
-                      f"elementwise work single-threaded"}
+    what = f"the whole M={M} batch" if tokens is None else f"{n} of the M={M} tokens (routing all {M})"
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except Exception:
+        nproc = os.cpu_count()
+    return {"value": n / med, "unit": "tok/s", "cores": blas or 1, "kind": "oracle",
+            "os_cpu_count": os.cpu_count(), "nproc": nproc, "blas_threads": blas,
+            "runs": runs, "median_s": med, "run_s": times,
+            "sample": f"median of {runs} oracle forwards of {what}: route, fp32 dequant of the "
+                      f"touched experts, fp64 SwiGLU MLPs, combine; numpy, matmuls on "
+                      f"{blas} BLAS threads (`cores`), elementwise work single-threaded"}
+
+
+def workload_record(w, r, decode, args, steps):
+    """The fields one workload contributes to the JSON line."""
+    ms = r["ms_per_step"]
+    src = source_hash("decode.hip" if decode else "prefill.hip", "device_common.h")
+    rec = {"workload": r["desc"], "M": w.M, "ms_per_step": ms, "tok_per_s": w.M / (ms * 1e-3),
+           "steps": steps, "weight_copies_rotated": r["copies"],
+           "hbm_gbps": r["layer_bytes"] / (ms * 1e-3) / 1e9,
+           "hbm_frac_layer": r["layer_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "tflops": r["flops"] / (ms * 1e-3) / 1e12,
+           "mfma_frac_layer": r["flops"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+           "layer_bytes_per_step": r["layer_bytes"], "flops_per_step": r["flops"],
+           "touched_experts": r["touched_experts"],
+           "stage_us": dict(zip(["route", "w13", "w2", "combine"], [round(v, 2) for v in r["stage_us"]])),
+           "roofline": roofline(w, r, src, decode)}
+    if not decode:
+        rec["block_m"] = r["block_m"]
+    return rec
 
 
 def repack_bench(steps: int, warmup: int) -> dict:
@@ -309,13 +387,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="qwen_decode",
-                    choices=["qwen_decode", "glm_decode", "glm_prefill", "glm_mxfp4", "glm_uniform"])
+    ap.add_argument("--workload", default=None,
+                    choices=["qwen_decode", "glm_decode", "glm_prefill", "glm_mxfp4", "glm_uniform"],
+                    help="run this workload alone (default: Qwen-shaped decode M=8 with its sweep, "
+                         "and GLM-class prefill M=4096)")
     ap.add_argument("--m", type=int, default=None, help="override the batch size")
     ap.add_argument("--copies", type=int, default=None, help="weight copies to rotate")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1,2,4 decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", type=int, default=None, metavar="MIB",
                     help="only copy MIB mebibytes device to device five times (the plain copy "
                          "the HBM traffic counters are scaled by) and exit")
@@ -354,10 +433,12 @@ def main():
     import weight_only_quantized_moe_amd as hm
     hm.load_library()
 
-    w = workload(args.workload, args.m)
+    default = args.workload is None
+    w = workload(args.workload or "qwen_decode", args.m)
     decode = w.M <= hm.DECODE_MAX_M
     log(f"measuring {w.name} (M={w.M}), {args.steps} steps after {args.warmup} warm-up")
     r = measure(w, args.steps, args.warmup, args.copies, block_m=args.block_m)
+    rec = workload_record(w, r, decode, args, args.steps)
     ms = r["ms_per_step"]
     out = {
         "metric": METRIC,
@@ -375,53 +456,57 @@ def main():
         "config": {"workload": r["desc"], "M": w.M, "tokens_per_step": w.M,
                    "weight_copies_rotated": r["copies"], "launch": "hip_graph_replay",
                    "parallelism": "single_gpu"},
-        "hbm_gbps": r["layer_bytes"] / (ms * 1e-3) / 1e9,
-        "layer_bytes_per_step": r["layer_bytes"],
-        "stage_us": dict(zip(["route", "w13", "w2", "combine"], [round(v, 2) for v in r["stage_us"]])),
+        "hbm_gbps": rec["hbm_gbps"],
+        "hbm_frac_layer": rec["hbm_frac_layer"],
+        "layer_bytes_per_step": rec["layer_bytes_per_step"],
+        "stage_us": rec["stage_us"],
+        "roofline": rec["roofline"],
     }
-    src = source_hash("decode.hip" if decode else "prefill.hip", "device_common.h")
     if decode:
-        t_w13 = r["w13_launch_us"] * 1e-6
-        achieved = r["w13_bytes"] / t_w13 / 1e9
-        out["distinct_experts"] = r["distinct_experts"]
-        out["roofline"] = {"bound": "hbm", "kernel": "gemv_kernel<W13> (decode W13 + SwiGLU)",
-                           "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": achieved / HBM_PEAK_GBPS, "algorithmic_bytes": r["w13_bytes"],
-                           "avg_launch_us": r["w13_launch_us"],
-                           "traffic": pmc_traffic("decode_w13_" + w.name, src, r["w13_bytes"])}
         out["config"]["distinct_experts"] = r["distinct_experts"]
     else:
-        t_w13 = r["w13_launch_us"] * 1e-6
-        achieved = r["w13_flops"] / t_w13 / 1e12
-        out["tflops"] = r["flops"] / (ms * 1e-3) / 1e12
-        out["roofline"] = {"bound": "mfma", "kernel": "grouped_gemm_kernel<W13> (prefill W13 + SwiGLU)",
-                           "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": r["w13_flops"],
-                           "avg_launch_us": r["w13_launch_us"],
-                           "traffic": pmc_traffic("prefill_w13_" + w.name, src, None)}
+        out["tflops"] = rec["tflops"]
+        out["mfma_frac_layer"] = rec["mfma_frac_layer"]
         out["config"]["touched_experts"] = r["touched_experts"]
         out["config"]["block_m"] = r["block_m"]
-    if decode and args.workload == "qwen_decode" and not args.no_sweep and args.m is None:
+    if decode and w.name.startswith("qwen_decode") and not args.no_sweep and args.m is None:
         sweep = []
         for m in (1, 2, 4):
-            wm = workload(args.workload, m)
+            wm = workload("qwen_decode", m)
             rm = measure(wm, args.steps, args.warmup, args.copies, packed=r["packed"])
-            sweep.append({"M": m, "tok_per_s": m / (rm["ms_per_step"] * 1e-3),
-                          "ms_per_step": rm["ms_per_step"],
-                          "hbm_gbps": rm["layer_bytes"] / (rm["ms_per_step"] * 1e-3) / 1e9,
-                          "w13_frac_of_hbm_peak": rm["w13_bytes"] / (rm["w13_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            rr = workload_record(wm, rm, True, args, args.steps)
+            sweep.append({"M": m, "tok_per_s": rr["tok_per_s"], "ms_per_step": rr["ms_per_step"],
+                          "hbm_gbps": rr["hbm_gbps"], "hbm_frac_layer": rr["hbm_frac_layer"],
+                          "w13_frac_of_hbm_peak": rr["roofline"]["frac_hip_events"],
                           "distinct_experts": rm["distinct_experts"]})
         sweep.append({"M": w.M, "tok_per_s": out["value"], "ms_per_step": ms, "hbm_gbps": out["hbm_gbps"],
-                      "w13_frac_of_hbm_peak": out["roofline"]["frac"], "distinct_experts": r["distinct_experts"]})
+                      "hbm_frac_layer": out["hbm_frac_layer"],
+                      "w13_frac_of_hbm_peak": out["roofline"]["frac_hip_events"],
+                      "distinct_experts": r["distinct_experts"]})
         out["sweep"] = sweep
     if not args.no_cpu_baseline:
         x_bits, logits = r["inputs"]
         log("timing the CPU oracle")
-        cb = cpu_baseline(r["packed"], x_bits, logits, args.cpu_budget,
-                          tokens=None if decode else [0, 1])
+        cb = cpu_baseline(r["packed"], x_bits, logits, 5 if decode else 3,
+                          tokens=None if decode else [0])
         if not decode:
             cb["value_tflops"] = r["flops"] * cb["value"] / w.M / 1e12
         out["cpu_baseline"] = cb
+    del r
+    if default:
+        # the prefill half of the metric: the GLM-class layer at M = 4096
+        wp = workload("glm_prefill", None)
+        psteps = max(5, min(args.steps, 100))
+        log(f"measuring {wp.name} (M={wp.M}), {psteps} steps after {min(args.warmup, 10)} warm-up")
+        rp = measure(wp, psteps, min(args.warmup, 10), args.copies)
+        prec = workload_record(wp, rp, False, args, psteps)
+        if not args.no_cpu_baseline:
+            x_bits, logits = rp["inputs"]
+            log("timing the CPU oracle (prefill sample)")
+            cb = cpu_baseline(rp["packed"], x_bits, logits, 3, tokens=[0])
+            cb["value_tflops"] = rp["flops"] * cb["value"] / wp.M / 1e12
+            prec["cpu_baseline"] = cb
+        out["prefill"] = prec
     print(json.dumps(out), flush=True)
 
 
