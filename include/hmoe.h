@@ -241,6 +241,21 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
                                uint16_t* y, void* scratch, size_t scratch_bytes,
                                hipStream_t stream);
 
+/* hybrid_moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc): the same kernels,
+ * with the scratch taken from a fixed 64 MiB array in the library's device memory, one
+ * per GPU, held until the process ends (its address is looked up with
+ * hipGetSymbolAddress on the first call on each device; the current device must be the
+ * stream's). Allocates nothing. All calls on one GPU share that GPU's array, so calls
+ * that overlap in time on one GPU (other streams, other threads) race; serialise them.
+ * Arguments and results as hybrid_moe_forward.
+ * Errors: HMOE_ERR_SCRATCH when moe_scratch_bytes(layer) exceeds 64 MiB (checked before
+ * any device call), HMOE_ERR_HIP when the array's address cannot be obtained, and the
+ * errors of hybrid_moe_forward. */
+hmoe_status hybrid_moe_forward_static(const hmoe_layer* layer, const hmoe_weights* weights,
+                                      const uint16_t* x, const float* router_logits, int32_t M,
+                                      uint16_t* y, hipStream_t stream);
+
 /* One stage of hybrid_moe_forward, for profiling: with the same arguments, calling
  * HMOE_STAGE_ROUTE, _W13, _W2 and _COMBINE in that order on one stream is exactly
  * hybrid_moe_forward. ROUTE is routing plus the per-slot pass records (M <= 8) or

@@ -154,3 +154,15 @@ def test_repack_argument_errors_without_launching():
     src = (hm.ExpertSrc * 8)()
     assert lib.moe_repack(layer.handle, src, ctypes.byref(w), None) == INVALID
     assert lib.moe_repack(None, src, ctypes.byref(w), None) == INVALID
+
+
+def test_static_forward_rejects_layers_beyond_its_scratch():
+    """hybrid_moe_forward_static checks the layer's scratch plan against its fixed array
+    before any device call: a GLM-class prefill layer (hundreds of MiB) is refused."""
+    lib = hm.load_library()
+    layer = hm.moe_layer_create(256, 6144, 2048, 8, 4096)
+    assert hm.moe_scratch_bytes(layer) > (64 << 20)
+    w = hm.Weights()
+    st = lib.hybrid_moe_forward_static(layer.handle, ctypes.byref(w), None, None, 16, None, None)
+    assert st == SCRATCH
+    assert "static scratch" in hm.moe_last_error()

@@ -27,7 +27,8 @@ DECODE_MAX_M = 8
 EXPORTED = (
     "moe_layer_create", "moe_layer_destroy", "moe_layer_query", "moe_scratch_bytes",
     "moe_route", "moe_align", "moe_align_view", "moe_decode_view", "moe_topk_view",
-    "hybrid_moe_forward", "hybrid_moe_forward_stage", "moe_dequant", "moe_repack",
+    "hybrid_moe_forward", "hybrid_moe_forward_static", "hybrid_moe_forward_stage", "moe_dequant",
+    "moe_repack",
     "moe_status_string", "moe_last_error",
 )
 
@@ -106,6 +107,9 @@ def load_library() -> ctypes.CDLL:
     lib.hybrid_moe_forward.argtypes = [c_void_p, POINTER(Weights), c_void_p, c_void_p, c_int32,
                                        c_void_p, c_void_p, c_size_t, c_void_p]
     lib.hybrid_moe_forward.restype = st
+    lib.hybrid_moe_forward_static.argtypes = [c_void_p, POINTER(Weights), c_void_p, c_void_p,
+                                              c_int32, c_void_p, c_void_p]
+    lib.hybrid_moe_forward_static.restype = st
     lib.hybrid_moe_forward_stage.argtypes = [c_void_p, POINTER(Weights), c_void_p, c_void_p, c_int32,
                                              c_void_p, c_void_p, c_size_t, c_int32, c_void_p]
     lib.hybrid_moe_forward_stage.restype = st
@@ -255,6 +259,16 @@ def hybrid_moe_forward(layer: Layer, weights: "DeviceWeights", x, router_logits,
     _check(load_library().hybrid_moe_forward(
         layer.handle, byref(weights.struct), _ptr(x), _ptr(router_logits), M, _ptr(y),
         _ptr(scratch), scratch.numel() * scratch.element_size(), _stream(stream)))
+
+
+def hybrid_moe_forward_static(layer: Layer, weights: "DeviceWeights", x, router_logits, y,
+                              stream=None) -> None:
+    """hybrid_moe_forward with the library's static per-GPU scratch: allocates nothing;
+    calls that overlap on one GPU race (see include/hmoe.h)."""
+    M = x.shape[0]
+    _check(load_library().hybrid_moe_forward_static(
+        layer.handle, byref(weights.struct), _ptr(x), _ptr(router_logits), M, _ptr(y),
+        _stream(stream)))
 
 
 def hybrid_moe_forward_stage(layer: Layer, weights: "DeviceWeights", x, router_logits, y, scratch,

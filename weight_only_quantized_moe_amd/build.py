@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "route.hip", "align.hip", "decode.hip", "prefill.hip", "dequant.hip",
-           "repack.hip"]
+           "repack.hip", "noalloc.hip"]
 # the streaming kernels must keep every value in registers: private-memory (scratch)
 # traffic shares the vector memory counter with the prefetched loads and drains them
 NO_SCRATCH = {"decode.hip", "prefill.hip"}

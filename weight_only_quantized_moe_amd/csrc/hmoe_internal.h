@@ -105,6 +105,11 @@ hipError_t launch_repack(RepackBatch& b, hipStream_t s);
 
 TierMask make_tier_mask(const Layer& L);
 
+// noalloc.hip: this device's file-scope scratch array (address looked up once per
+// device) and its size
+hipError_t static_scratch(void** out);
+size_t static_scratch_bytes();
+
 bool plan_gemv(int K, GemvTiling* t);
 
 }  // namespace hmoe

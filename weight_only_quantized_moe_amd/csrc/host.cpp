@@ -354,6 +354,21 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
   return HMOE_OK;
 }
 
+hmoe_status hybrid_moe_forward_static(const hmoe_layer* layer, const hmoe_weights* weights,
+                                      const uint16_t* x, const float* router_logits, int32_t M,
+                                      uint16_t* y, hipStream_t stream) {
+  if (hmoe_status st = check_layer(layer)) return st;
+  const size_t need = layer->L.plan.total, have = hmoe::static_scratch_bytes();
+  if (need > have)
+    return fail(HMOE_ERR_SCRATCH, "the layer needs " + std::to_string(need) +
+                                      " bytes of scratch, the static scratch holds " +
+                                      std::to_string(have) + ": use hybrid_moe_forward");
+  void* scratch = nullptr;
+  hipError_t err = hmoe::static_scratch(&scratch);
+  if (err != hipSuccess) return hip_fail(err, "static scratch address");
+  return hybrid_moe_forward(layer, weights, x, router_logits, M, y, scratch, have, stream);
+}
+
 hmoe_status moe_dequant(const hmoe_layer* layer, const hmoe_weights* weights, int32_t expert,
                         int32_t tensor, float* out_f32, uint16_t* out_bf16, hipStream_t stream) {
   if (hmoe_status st = check_layer(layer)) return st;
