@@ -106,7 +106,8 @@ def pmc_traffic(kernel_key, src_hash, launches_bytes):
         return None
 
 
-def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=None):
+def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=None,
+            decode_launch=0):
     """Times `steps` graph replays of the forward at w.M; returns a result dict."""
     import numpy as np
     import torch
@@ -120,7 +121,7 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
         log(f"{w.name}: generated packed layer in {time.time() - t0:.1f}s")
     bm = packed["bit_map"]
     fmt = hm.KEPT_NVFP4 if packed["kept_format"] == "nvfp4" else hm.KEPT_MXFP4
-    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, block_m or 0)
+    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, block_m or 0, decode_launch)
     block_m = hm.moe_layer_query(layer)["block_m"]
     base = hm.DeviceWeights(packed)
     layer_bytes = base.nbytes()
@@ -186,11 +187,25 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
     torch.cuda.synchronize()
     w13_launch_us = k0.elapsed_time(k1) * 1e3 / reps
 
+    # the single-launch decode alone (M <= 8 on layers that have it): back-to-back
+    # forwards, each one launch, between two events on the launch stream
+    fused = bool(hm.moe_layer_query(layer)["fused_decode"]) and w.M <= hm.DECODE_MAX_M
+    fused_launch_us = None
+    if fused:
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(1e8))
+        k0.record()
+        for i in range(reps):
+            hm.hybrid_moe_forward(layer, wts[i % copies], x, lg, y, scratch)
+        k1.record()
+        torch.cuda.synchronize()
+        fused_launch_us = k0.elapsed_time(k1) * 1e3 / reps
+
     # algorithmic work from the routing this batch produced
     eb = expert_bytes(packed)
     k, M = w.top_k, w.M
     res = {"ms_per_step": ms_per_step, "stage_us": stage_us, "copies": copies, "block_m": block_m,
-           "w13_launch_us": w13_launch_us,
+           "w13_launch_us": w13_launch_us, "fused_launch_us": fused_launch_us,
            "layer_bytes_resident": layer_bytes, "desc": describe(w, packed)}
     io_bytes = M * w.H * 2 + M * w.E * 4 + M * w.H * 2        # x, logits, y
     flops = 6.0 * M * k * w.H * w.I
@@ -239,19 +254,24 @@ def rocprof_launch_us(kernel_key, src_hash):
 
 
 def roofline(w, r, src, decode):
-    """Roofline of the dominant kernel (the W13 stage). The bound follows the layer's
-    arithmetic intensity (flops per algorithmic byte) against the ridge point of the
-    peaks."""
+    """Roofline of the dominant kernel: the single-launch decode kernel (the whole
+    step: every algorithmic byte of the layer) where the layer has it, else the W13
+    stage. The bound follows the layer's arithmetic intensity (flops per algorithmic
+    byte) against the ridge point of the peaks."""
     intensity = r["flops"] / r["layer_bytes"]
     hbm = decode or intensity < RIDGE_FLOP_PER_BYTE
-    key = ("decode_w13_" if decode else "prefill_w13_") + w.name
-    if hbm:
+    fused = decode and r.get("fused_launch_us") is not None
+    key = ("decode_fused_" if fused else "decode_w13_" if decode else "prefill_w13_") + w.name
+    if fused:
+        work, scale, peak, unit = r["layer_bytes"], 1e9, HBM_PEAK_GBPS, "GB/s"
+    elif hbm:
         work, scale, peak, unit = r["w13_bytes"], 1e9, HBM_PEAK_GBPS, "GB/s"
     else:
         work, scale, peak, unit = r["w13_flops"], 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
-    kernel = ("w13_gemv_kernel (decode W13 + SwiGLU)" if decode
+    kernel = ("decode_fused_kernel (the whole decode forward)" if fused
+              else "w13_gemv_kernel (decode W13 + SwiGLU)" if decode
               else "grouped_gemm_kernel<W13> (prefill W13 + SwiGLU)")
-    ev_us = r["w13_launch_us"]
+    ev_us = r["fused_launch_us"] if fused else r["w13_launch_us"]
     prof_us, prof = rocprof_launch_us(key, src)
     us = prof_us if prof_us is not None else ev_us
     achieved = work / (us * 1e-6) / scale
@@ -469,6 +489,15 @@ def main():
         out["mfma_frac_layer"] = rec["mfma_frac_layer"]
         out["config"]["touched_experts"] = r["touched_experts"]
         out["config"]["block_m"] = r["block_m"]
+    if decode:
+        # the same batch with the decode forward as one persistent launch
+        rs = measure(w, args.steps, args.warmup, args.copies, packed=r["packed"], decode_launch=1)
+        out["single_launch"] = {
+            "kernel": "decode_fused_kernel (routing, W13 + SwiGLU, W2, combine in one launch)",
+            "ms_per_step": rs["ms_per_step"], "tok_per_s": w.M / (rs["ms_per_step"] * 1e-3),
+            "hbm_frac_layer": rs["layer_bytes"] / (rs["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "avg_launch_us_hip_events": rs["fused_launch_us"],
+            "default_ms_per_step": ms}
     if decode and w.name.startswith("qwen_decode") and not args.no_sweep and args.m is None:
         sweep = []
         for m in (1, 2, 4):

@@ -61,6 +61,8 @@ typedef enum hmoe_status {
 } hmoe_status;
 
 enum { HMOE_KEPT_NVFP4 = 0, HMOE_KEPT_MXFP4 = 1 };
+/* How hybrid_moe_forward runs the decode path (M <= 8). */
+enum { HMOE_DECODE_STAGED = 0, HMOE_DECODE_SINGLE_LAUNCH = 1 };
 enum { HMOE_TIER_KEPT = 0, HMOE_TIER_NF3 = 1 };
 enum { HMOE_TENSOR_W13 = 0, HMOE_TENSOR_W2 = 1 };
 /* Stages of the forward, in launch order (see hybrid_moe_forward_stage). */
@@ -83,7 +85,12 @@ enum { HMOE_STAGE_ROUTE = 0, HMOE_STAGE_W13 = 1, HMOE_STAGE_W2 = 2, HMOE_STAGE_C
  *   block_m      prefill rows per expert block for moe_align: 16, 32, 64 or 128; 0 lets
  *                the library pick from t = max_tokens * top_k / E: 16 below t = 4, 32
  *                below 24, else 128. The prefill GEMM runs a block whose real slots
- *                fit in 16, 32 or 64 rows as a tile of that many rows. */
+ *                fit in 16, 32 or 64 rows as a tile of that many rows.
+ *   decode_launch HMOE_DECODE_STAGED (0): the decode path as four kernels (routing, W13,
+ *                W2, combine), the faster form on MI355X at every measured shape;
+ *                HMOE_DECODE_SINGLE_LAUNCH (1): the whole decode forward in one
+ *                persistent kernel ([P1] "How it works": the M <= 8 direct top-k path);
+ *                both give the same bits. */
 typedef struct hmoe_layer_desc {
     int32_t num_experts;
     int32_t hidden;
@@ -93,6 +100,7 @@ typedef struct hmoe_layer_desc {
     int32_t kept_format;
     const uint8_t* bit_map;
     int32_t block_m;
+    int32_t decode_launch;
 } hmoe_layer_desc;
 
 /* Opaque, immutable after creation: concurrent calls on different streams with
@@ -107,6 +115,8 @@ typedef struct hmoe_layer_info {
     int32_t block_m;           /* effective block_m */
     int32_t max_distinct;      /* min(8 * top_k, E): decode group capacity */
     int32_t cap_kept, cap_nf3; /* align capacity per tier at max_tokens */
+    int32_t fused_decode;      /* 1: hybrid_moe_forward runs M <= 8 as one launch */
+    int32_t single_launch_available; /* 1: a single-launch decode exists for H and I */
 } hmoe_layer_info;
 
 /* Packed weights of both tiers, in the layouts above. Device pointers, owned by the
@@ -160,9 +170,13 @@ typedef struct hmoe_align_view {
  *   slots       int32 [max_distinct, 8]: those slots, ascending
  *   expert_tier int32 [E]: (tier << 16) | tier-local id of every expert
  *   passes      int32 [M * k, 4]: one record per slot, in slot order: (slot,
- *               (tier << 16) | tier-local id, token, expert); the decode GEMVs split
- *               their work over these records (written by the ROUTE stage; the other
- *               fields by the COMBINE stage, off the critical path) */
+ *               (tier << 16) | tier-local id, token, expert); the staged decode GEMVs
+ *               split their work over these records (written by the ROUTE stage; the
+ *               other fields by the COMBINE stage, off the critical path; the single
+ *               launch writes all of them from a block of its own)
+ *   sync_timeouts int32 [1]: how many bounded waits of the single-launch decode gave up
+ *               (cumulative over the scratch's life; 0 unless its grid could not be
+ *               resident at once, e.g. beside another persistent kernel) */
 typedef struct hmoe_decode_view {
     int32_t* counts;
     int32_t* experts;
@@ -171,14 +185,16 @@ typedef struct hmoe_decode_view {
     int32_t* expert_tier;
     int32_t* passes;
     int32_t max_distinct;
+    int32_t* sync_timeouts;
 } hmoe_decode_view;
 
 /* Creates a layer from a descriptor (host only; no device call). *out receives a
  * handle owned by the library until moe_layer_destroy.
  * Errors: HMOE_ERR_INVALID_ARG (null pointers, E < 1, k < 1, k > E, max_tokens < 1,
- * a bit map value other than 3 or 4, an unknown kept format or block_m);
+ * a bit map value other than 3 or 4, an unknown kept format, block_m or decode_launch);
  * HMOE_ERR_UNSUPPORTED (E > 1024, k > 16, H or I not a multiple of 128, a K for
- * which no decode tiling exists, max_tokens * top_k > 2^24, max_tokens * H or the
+ * which no decode tiling exists, HMOE_DECODE_SINGLE_LAUNCH for an H and I it is not built
+ * for (see single_launch_available), max_tokens * top_k > 2^24, max_tokens * H or the
  * prefill h rows * I reaching 2^31, or a prefill GEMM grid of 2^31 blocks or more
  * at max_tokens). */
 hmoe_status moe_layer_create(const hmoe_layer_desc* desc, hmoe_layer** out);
@@ -197,6 +213,14 @@ hmoe_status moe_layer_query(const hmoe_layer* layer, hmoe_layer_info* out);
  * outputs [max_tokens * k, H] (fp32); each region is 256-byte aligned. The caller
  * allocates the buffer and passes it to every call. */
 hmoe_status moe_scratch_bytes(const hmoe_layer* layer, size_t* bytes);
+
+/* Prepares a scratch buffer for its first forward: zero-fills the counters the
+ * single-launch decode synchronises its workgroups with (every forward leaves them
+ * zero again). A scratch buffer that was allocated zero-filled needs no call. Enqueued on
+ * `stream` (a fill kernel, no memset, so it may be captured).
+ * Errors: HMOE_ERR_INVALID_ARG, HMOE_ERR_ALIGN, HMOE_ERR_SCRATCH, HMOE_ERR_HIP. */
+hmoe_status moe_scratch_init(const hmoe_layer* layer, void* scratch, size_t scratch_bytes,
+                             hipStream_t stream);
 
 /* Softmax top-k routing, renormalised. logits: fp32 [M, E] (device). For each token,
  * experts are ranked by logit, descending, ties to the lower expert id; topk_ids
@@ -230,10 +254,13 @@ hmoe_status moe_topk_view(const hmoe_layer* layer, void* scratch, int32_t** topk
 /* The layer forward ([P1] "How it works", [P2] "Summary"): y = sum over each token's
  * top-k experts of w[t, j] * SwiGLU_expert(x[t]), both tiers sharing one routing result
  * and one sum. x: bf16 bits [M, H]; router_logits: fp32 [M, E]; y: bf16 bits [M, H],
- * fully overwritten. M <= 8 takes the decode path (route + pass records, W13 + SwiGLU,
- * W2 + weighted combine); M > 8 the prefill path (route, per-tier align, grouped GEMM W13 +
+ * fully overwritten. M <= 8 takes the decode path: the four launches of
+ * hybrid_moe_forward_stage, or, for a layer created with HMOE_DECODE_SINGLE_LAUNCH, one
+ * launch (routing in every workgroup, W13 + SwiGLU, W2, and the weighted combine by
+ * whichever workgroup finishes a 64-row output group last); both give the same bits. M > 8 takes the prefill path (route, per-tier align, grouped GEMM W13 +
  * SwiGLU, grouped GEMM W2 + weighted combine). M = 0 is a no-op returning HMOE_OK.
  * Never allocates, synchronises or reads back: capturable in a HIP graph at fixed M.
+ * The scratch must have been zero-filled or passed through moe_scratch_init once.
  * Errors: HMOE_ERR_INVALID_ARG (null layer/weights, M < 0, a needed weight array NULL),
  * HMOE_ERR_CAPACITY, HMOE_ERR_SCRATCH, HMOE_ERR_ALIGN, HMOE_ERR_HIP. */
 hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weights,
@@ -256,9 +283,10 @@ hmoe_status hybrid_moe_forward_static(const hmoe_layer* layer, const hmoe_weight
                                       const uint16_t* x, const float* router_logits, int32_t M,
                                       uint16_t* y, hipStream_t stream);
 
-/* One stage of hybrid_moe_forward, for profiling: with the same arguments, calling
- * HMOE_STAGE_ROUTE, _W13, _W2 and _COMBINE in that order on one stream is exactly
- * hybrid_moe_forward. ROUTE is routing plus the per-slot pass records (M <= 8) or
+/* One stage of the forward, for profiling: with the same arguments, calling
+ * HMOE_STAGE_ROUTE, _W13, _W2 and _COMBINE in that order on one stream computes what
+ * hybrid_moe_forward computes, bit for bit (for M <= 8 as four launches where the forward
+ * may use one). ROUTE is routing plus the per-slot pass records (M <= 8) or
  * routing, the per-tier align and the tokens' conversion to scaled fp16 (M > 8); W13 is
  * the expert up projection with the fused SwiGLU; W2 the down projection with the
  * routing weight; COMBINE the fixed-order top-k sum into y (plus, for M <= 8, the

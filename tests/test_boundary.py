@@ -54,6 +54,8 @@ def _create_status(**kw):
     ({"max_tokens": 0}, INVALID),
     ({"kept_format": 7}, INVALID),
     ({"block_m": 48}, INVALID),
+    ({"decode_launch": 2}, INVALID),
+    ({"hidden": 128, "inter": 128, "decode_launch": 1}, UNSUPPORTED),
     ({"bit_map": [4, 3, 5, 3, 3, 3, 3, 3]}, INVALID),
     ({"num_experts": 2048, "top_k": 2}, UNSUPPORTED),
     ({"num_experts": 32, "top_k": 17}, UNSUPPORTED),

@@ -129,6 +129,77 @@ def test_qwen_decode_full(hm, qwen, M):
     check_output(y, OL.forward(packed, x, lg)["y"], f"qwen decode M={M}")
 
 
+def _staged(hm, layer, wts, x, lg, scratch):
+    torch = torch_mod()
+    y = torch.full((x.shape[0], x.shape[1]), 0x7FC0, dtype=torch.int16, device="cuda")
+    for st in (hm.STAGE_ROUTE, hm.STAGE_W13, hm.STAGE_W2, hm.STAGE_COMBINE):
+        hm.hybrid_moe_forward_stage(layer, wts, x, lg, y, scratch, st)
+    return y
+
+
+@pytest.mark.parametrize("case", ["tiny_nvfp4", "tiny_mxfp4", "qwen", "glm"])
+def test_single_launch_decode_matches_staged(hm, qwen, case):
+    """The one-launch decode forward against the four-launch stages on the same inputs:
+    y, top-k ids and weights and pass records bit-identical, at M = 1, 3, 8, three calls
+    in a row on one scratch (the counters it synchronises with must return to zero), no
+    bounded wait given up."""
+    torch = torch_mod()
+    if case == "qwen":
+        w, packed, wts = qwen
+    elif case == "glm":
+        w = synth.glm_decode(8)
+        packed = synth.packed_layer(w)
+        wts = hm.DeviceWeights(packed)
+    else:
+        packed, w = tiny_packed(case.split("_")[1], "prefix")
+        wts = hm.DeviceWeights(packed)
+    layer = make_layer(packed, 8, 0, hm.DECODE_SINGLE_LAUNCH)
+    assert hm.moe_layer_query(layer)["fused_decode"] == 1
+    s_fused, s_staged = scratch_for(layer), scratch_for(layer)
+    for M in (1, 3, 8, 8):
+        x = to_dev_bits(synth.activations_bf16(w, M))
+        lg = to_dev(synth.router_logits(w, M))
+        y = torch.full((M, w.H), 0x7FC0, dtype=torch.int16, device="cuda")
+        hm.hybrid_moe_forward(layer, wts, x, lg, y, s_fused)
+        y_st = _staged(hm, layer, wts, x, lg, s_staged)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_st), f"{case} M={M}: single launch differs from the stages"
+        for name in ("passes",):
+            a = hm.moe_decode_view(layer, s_fused)[name][:M * w.top_k]
+            b = hm.moe_decode_view(layer, s_staged)[name][:M * w.top_k]
+            assert torch.equal(a, b), f"{case} M={M}: {name}"
+        ia, wa = hm.moe_topk_view(layer, s_fused, M)
+        ib, wb = hm.moe_topk_view(layer, s_staged, M)
+        assert torch.equal(ia, ib) and torch.equal(wa, wb), f"{case} M={M}: top-k"
+        assert int(hm.moe_decode_view(layer, s_fused)["sync_timeouts"][0]) == 0
+    if case == "qwen":
+        # HIP graph replays of the single launch, eager calls in between
+        M = 4
+        x = to_dev_bits(synth.activations_bf16(w, M))
+        lg = to_dev(synth.router_logits(w, M))
+        y_ref = _staged(hm, layer, wts, x, lg, s_staged)
+        y = torch.zeros((M, w.H), dtype=torch.int16, device="cuda")
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                hm.hybrid_moe_forward(layer, wts, x, lg, y, s_fused)
+        torch.cuda.synchronize()
+        for rep in range(4):
+            y.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_ref), f"replay {rep} differs"
+            y2 = torch.empty_like(y)
+            hm.hybrid_moe_forward(layer, wts, x, lg, y2, s_fused)
+            torch.cuda.synchronize()
+            assert torch.equal(y2, y_ref)
+        assert int(hm.moe_decode_view(layer, s_fused)["sync_timeouts"][0]) == 0
+    del wts
+    torch.cuda.empty_cache()
+
+
 def test_qwen_prefill_small(hm, qwen):
     w, packed, wts = qwen
     M = 48

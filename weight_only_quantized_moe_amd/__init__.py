@@ -19,6 +19,7 @@ from ctypes import POINTER, Structure, byref, c_char_p, c_int32, c_size_t, c_voi
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhmoe.so")
 
 KEPT_NVFP4, KEPT_MXFP4 = 0, 1
+DECODE_STAGED, DECODE_SINGLE_LAUNCH = 0, 1
 TIER_KEPT, TIER_NF3 = 0, 1
 TENSOR_W13, TENSOR_W2 = 0, 1
 STAGE_ROUTE, STAGE_W13, STAGE_W2, STAGE_COMBINE = 0, 1, 2, 3
@@ -26,6 +27,7 @@ DECODE_MAX_M = 8
 
 EXPORTED = (
     "moe_layer_create", "moe_layer_destroy", "moe_layer_query", "moe_scratch_bytes",
+    "moe_scratch_init",
     "moe_route", "moe_align", "moe_align_view", "moe_decode_view", "moe_topk_view",
     "hybrid_moe_forward", "hybrid_moe_forward_static", "hybrid_moe_forward_stage", "moe_dequant",
     "moe_repack",
@@ -42,13 +44,14 @@ class HmoeError(RuntimeError):
 class LayerDesc(Structure):
     _fields_ = [("num_experts", c_int32), ("hidden", c_int32), ("inter", c_int32),
                 ("top_k", c_int32), ("max_tokens", c_int32), ("kept_format", c_int32),
-                ("bit_map", c_void_p), ("block_m", c_int32)]
+                ("bit_map", c_void_p), ("block_m", c_int32), ("decode_launch", c_int32)]
 
 
 class LayerInfo(Structure):
     _fields_ = [(n, c_int32) for n in (
         "num_experts", "hidden", "inter", "top_k", "max_tokens", "kept_format",
-        "num_kept", "num_nf3", "block_m", "max_distinct", "cap_kept", "cap_nf3")]
+        "num_kept", "num_nf3", "block_m", "max_distinct", "cap_kept", "cap_nf3",
+        "fused_decode", "single_launch_available")]
 
 
 class Weights(Structure):
@@ -70,7 +73,7 @@ class AlignView(Structure):
 class DecodeView(Structure):
     _fields_ = [("counts", c_void_p), ("experts", c_void_p), ("num_slots", c_void_p),
                 ("slots", c_void_p), ("expert_tier", c_void_p), ("passes", c_void_p),
-                ("max_distinct", c_int32)]
+                ("max_distinct", c_int32), ("sync_timeouts", c_void_p)]
 
 
 _lib = None
@@ -94,6 +97,8 @@ def load_library() -> ctypes.CDLL:
     lib.moe_layer_query.restype = st
     lib.moe_scratch_bytes.argtypes = [c_void_p, POINTER(c_size_t)]
     lib.moe_scratch_bytes.restype = st
+    lib.moe_scratch_init.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.moe_scratch_init.restype = st
     lib.moe_route.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
     lib.moe_route.restype = st
     lib.moe_align.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]
@@ -166,13 +171,14 @@ class Layer:
 
 
 def moe_layer_create(num_experts: int, hidden: int, inter: int, top_k: int, max_tokens: int,
-                     kept_format: int = KEPT_NVFP4, bit_map=None, block_m: int = 0) -> Layer:
+                     kept_format: int = KEPT_NVFP4, bit_map=None, block_m: int = 0,
+                     decode_launch: int = DECODE_STAGED) -> Layer:
     lib = load_library()
     bm = None
     if bit_map is not None:
         bm = (ctypes.c_uint8 * num_experts)(*[int(v) for v in bit_map])
     d = LayerDesc(num_experts, hidden, inter, top_k, max_tokens, kept_format,
-                  ctypes.cast(bm, c_void_p) if bm is not None else None, block_m)
+                  ctypes.cast(bm, c_void_p) if bm is not None else None, block_m, decode_launch)
     h = c_void_p()
     _check(lib.moe_layer_create(byref(d), byref(h)))
     return Layer(h, bm)
@@ -188,6 +194,13 @@ def moe_scratch_bytes(layer: Layer) -> int:
     n = c_size_t()
     _check(load_library().moe_scratch_bytes(layer.handle, byref(n)))
     return n.value
+
+
+def moe_scratch_init(layer: Layer, scratch, stream=None) -> None:
+    """Zero-fills the scratch's decode counters (not needed for a zero-filled buffer)."""
+    _check(load_library().moe_scratch_init(layer.handle, _ptr(scratch),
+                                           scratch.numel() * scratch.element_size(),
+                                           _stream(stream)))
 
 
 def moe_route(logits, top_k: int, topk_ids, topk_w, stream=None) -> None:
@@ -239,6 +252,7 @@ def moe_decode_view(layer: Layer, scratch) -> dict:
         "expert_tier": _scratch_view(scratch, v.expert_tier, E, torch.int32),
         # pass records of the first M * k slots of the last decode forward
         "passes": _scratch_view(scratch, v.passes, n_pass * 4, torch.int32).view(n_pass, 4),
+        "sync_timeouts": _scratch_view(scratch, v.sync_timeouts, 1, torch.int32),
     }
 
 

@@ -31,6 +31,7 @@
 
 #include "device_common.h"
 #include "hmoe_internal.h"
+#include "route_common.h"
 
 namespace hmoe {
 
@@ -55,6 +56,16 @@ struct GemvArgs {
   float* h_out;  // W13: fp32 [slots, I]
   float* o_out;  // W2: fp32 [slots, H]
 };
+
+// Agent-coherent (write-through) store and load of one fp32 value: the single-launch
+// decode hands h and the per-slot outputs from one workgroup to another, possibly on
+// another XCD, without cache-wide fences (see decode_fused_kernel).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Transposing reduction of V values per lane over aligned LR-lane segments (V <= LR,
 // both powers of two): each step keeps one half of the values and adds the partner
@@ -403,7 +414,7 @@ __device__ __forceinline__ void w13_load(const GemvArgs& a, int loc, int i0, W13
   }
 }
 
-template <int LR, int KU, int RI, int FMT>
+template <int LR, int KU, int RI, int FMT, bool COH = false>
 __device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, int slot, float g,
                                             const uint32_t (&x)[1][KU][16],
                                             const uint32_t* lut_lane, const W13Buf<KU, RI>& b) {
@@ -423,13 +434,16 @@ __device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, int slot,
   const float gate = seg_reduce<RI, LR>(vg) * g;
   const float up = seg_reduce<RI, LR>(vu) * g;
   const int ri = seg_index<RI, LR>(c);
-  if ((c & (LR / RI - 1)) == 0)
-    a.h_out[(size_t)slot * a.I + i0 + ri * P + rw] = silu(gate) * up;
+  if ((c & (LR / RI - 1)) == 0) {
+    float* out = a.h_out + (size_t)slot * a.I + i0 + ri * P + rw;
+    if constexpr (COH) store_coherent(out, silu(gate) * up);
+    else *out = silu(gate) * up;
+  }
 }
 
 // Chunks [c0, end) of one pass (chunk `first` is the expert's pair 0). A holds
 // chunk c0 on entry when a_loaded.
-template <int LR, int KU, int RI, int FMT>
+template <int LR, int KU, int RI, int FMT, bool COH = false>
 __device__ __forceinline__ void w13_pass(const GemvArgs& a, const PassInfo& pi, int c0, int end,
                                          int first, float g, const uint32_t* lut_lane,
                                          W13Buf<KU, RI>& A, W13Buf<KU, RI>& B, bool a_loaded) {
@@ -443,10 +457,10 @@ __device__ __forceinline__ void w13_pass(const GemvArgs& a, const PassInfo& pi, 
   // so that the wait counts before each compute are the same on every path
   while (cc < end) {
     w13_load<LR, KU, RI, FMT>(a, pi.loc, (min(cc + 1, end - 1) - first) * CH, B);
-    w13_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
+    w13_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
     if (++cc >= end) break;
     w13_load<LR, KU, RI, FMT>(a, pi.loc, (min(cc + 1, end - 1) - first) * CH, A);
-    w13_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
+    w13_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
     ++cc;
   }
 }
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
 // Stages the slot's h row in this wave's LDS region as fp16 pairs scaled by 2^-e (e
 // from the row's largest |h|, so the largest lands in [2^14, 2^15)), then reads this
 // lane's KU units into x. Returns e.
-template <int LR, int KU>
+template <int LR, int KU, bool COH = false>
 __device__ __forceinline__ int stage_h(const GemvArgs& a, int slot, uint32_t* hs, int c,
                                        uint32_t (&x)[1][KU][16]) {
   constexpr int NF4 = 8 * LR * KU;          // float4s per row (K = 32 * LR * KU)
@@ -517,7 +531,15 @@ __device__ __forceinline__ int stage_h(const GemvArgs& a, int slot, uint32_t* hs
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int f = lane + kWave * i;
-    v[i] = (NF4 % kWave == 0 || f < NF4) ? row[f] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if constexpr (COH) {
+      const float* r = reinterpret_cast<const float*>(row + f);
+      v[i] = (NF4 % kWave == 0 || f < NF4)
+                 ? make_float4(load_coherent(r), load_coherent(r + 1), load_coherent(r + 2),
+                               load_coherent(r + 3))
+                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else {
+      v[i] = (NF4 % kWave == 0 || f < NF4) ? row[f] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
     mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
   }
   mx = group_max<kWave>(mx);
@@ -569,7 +591,7 @@ __device__ __forceinline__ void w2_load(const GemvArgs& a, int loc, int n0, W2Bu
     load_row<LR, KU, FMT>(a, (size_t)loc * a.rows + n0 + ri * P + rw, c, b.q[ri], b.sc[ri]);
 }
 
-template <int LR, int KU, int RI, int FMT>
+template <int LR, int KU, int RI, int FMT, bool COH = false>
 __device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, int slot, float g,
                                            const uint32_t (&x)[1][KU][16],
                                            const uint32_t* lut_lane, const W2Buf<KU, RI>& b) {
@@ -586,10 +608,14 @@ __device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, int slot, 
   }
   const float sum = seg_reduce<RI, LR>(v);
   const int ri = seg_index<RI, LR>(c);
-  if ((c & (LR / RI - 1)) == 0) a.o_out[(size_t)slot * a.rows + n0 + ri * P + rw] = sum * g;
+  if ((c & (LR / RI - 1)) == 0) {
+    float* out = a.o_out + (size_t)slot * a.rows + n0 + ri * P + rw;
+    if constexpr (COH) store_coherent(out, sum * g);
+    else *out = sum * g;
+  }
 }
 
-template <int LR, int KU, int RI, int FMT>
+template <int LR, int KU, int RI, int FMT, bool COH = false>
 __device__ __forceinline__ void w2_pass(const GemvArgs& a, const PassInfo& pi, int c0, int end,
                                         int first, float gt, const uint32_t* lut_lane,
                                         uint32_t* hs, W2Buf<KU, RI>& A, W2Buf<KU, RI>& B,
@@ -599,13 +625,13 @@ __device__ __forceinline__ void w2_pass(const GemvArgs& a, const PassInfo& pi, i
   int cc = c0;
   if (!a_loaded) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc - first) * CH, A);
   uint32_t x[1][KU][16];
-  const float g = __builtin_ldexpf(gt, stage_h<LR, KU>(a, pi.slot, hs, c, x));
+  const float g = __builtin_ldexpf(gt, stage_h<LR, KU, COH>(a, pi.slot, hs, c, x));
   while (cc < end) {
     if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, B);
-    w2_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
+    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
     if (++cc >= end) break;
     if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, A);
-    w2_compute<LR, KU, RI, FMT>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
+    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
     ++cc;
   }
 }
@@ -780,6 +806,325 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 }
 
 // ---------------------------------------------------------------------------
+// Single-launch decode (M <= 8)
+// ---------------------------------------------------------------------------
+//
+// decode_fused_kernel runs the whole decode forward in one launch: routing, W13 +
+// SwiGLU, W2 and the weighted top-k combine (local-inference-lab/vllm PR #92, "How it
+// works": the M <= 8 path is addressed directly by the top-k result, and both tiers
+// share one routing and one top-k sum). The grid is persistent (as many blocks as are
+// resident at once). Blocks 0 .. G-2 are work blocks: each of their waves takes a
+// contiguous run of the flat W13 range (npass * per13 chunks), then one of the W2 range,
+// with the same chunk code as the four-launch path, so h, the per-slot outputs and y are
+// bit-identical to it. Every block routes all M tokens itself (one wave per token, the
+// rows requested before its level tables are built) and shares the result in LDS, so no
+// block waits for routing done elsewhere. The last block
+// routes every token once more and writes the inspection outputs (top-k ids and weights,
+// pass records, tier map, decode grouping) off the critical path.
+//
+// Hand-offs between workgroups go through counters in scratch, one 64-byte line each:
+//   h_cnt[s]      W13 chunks of slot s finished; the wave whose increment completes it
+//                 sets slot s's ready flag in all kReadyCopies copies;
+//   ready[s][c]   a W2 run of slot s first requests its weights, then polls copy
+//                 blockIdx % kReadyCopies of the flag (many waiters on one line slow
+//                 down every access to that memory channel, so they are spread out);
+//   comb[t][g]    W2 chunks of token t's 64-row output group g finished over all k slots;
+//                 the wave whose increment completes it sums the k slot rows in fixed slot
+//                 order and writes those 64 outputs of y;
+//   exit          blocks finished; the last one clears every counter, so each launch
+//                 starts from zeros (the scratch's sync region must be zero before the
+//                 first decode forward: moe_scratch_init, or a zero-filled allocation).
+// h and the per-slot outputs are written with agent-coherent (write-through) stores and
+// read with agent-coherent loads; before a counter increment the wave waits for all its
+// memory operations to complete, so the data it signals is visible on every XCD. This
+// avoids cache-wide release/acquire fences, which measured about 70 ns each, serialised
+// per XCD, on MI355X. Waits are bounded (kSpinLimit polls): a wait that gives up, which
+// only a grid that is not fully resident can cause, is counted in the sync region
+// (moe_decode_view's sync_timeouts) and the launch still ends.
+
+constexpr int kSyncLine = 16;                  // sync words per counter (one 64-byte line)
+constexpr int kSyncExit = 0;                   // blocks finished
+constexpr int kSyncTimeouts = kSyncLine;       // bounded waits that gave up (never cleared)
+constexpr int kSyncH = 2 * kSyncLine;          // h_cnt[s] at kSyncH + s * kSyncLine
+constexpr int kReadyCopies = 16;               // copies of each slot's ready flag
+constexpr int kCombRows = 64;                  // rows of y per combine group
+constexpr int kSpinLimit = 1 << 16;
+// gfx9 s_waitcnt operand: vmcnt 0 (every vector memory operation of the wave, its
+// coherent stores and atomics included, has completed), expcnt 7 and lgkmcnt 15 free
+constexpr int kWaitVmem = 0x0F70;
+
+struct FusedArgs {
+  GemvArgs a13, a2;
+  const float* logits;
+  int M, E, k;
+  int per13, per2;   // chunks per pass of each GEMV
+  int nwork;         // work waves (four per work block)
+  int nwork_blocks;
+  int G;             // combine groups per token: H / 64
+  int ready_base;    // word offset of ready[0][0]
+  int comb_base;     // word offset of comb[0][0]
+  uint32_t* sync;
+  const float* o;    // per-slot outputs (a2.o_out)
+  uint16_t* y;
+  int32_t* ids;      // inspection outputs, written by the last block
+  float* w;
+  int32_t* expert_tier;
+  int32_t* pass;
+  GroupArgs ga;
+};
+
+__device__ __forceinline__ uint32_t sync_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t sync_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sync_store(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// all of this wave's memory operations complete before anything after it is issued
+__device__ __forceinline__ void wait_vmem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The routing of every token, shared by a block's waves through LDS: slot s = t * k + j
+// routes to expert ids[s] with weight w[s].
+struct BlockRoute {
+  int32_t ids[kDecodeMaxM * kMaxTopK];
+  float w[kDecodeMaxM * kMaxTopK];
+};
+
+// calls f with NV (logits per lane for E experts) as a compile-time constant
+template <typename F>
+__device__ __forceinline__ void with_nv(int E, F&& f) {
+  if (E <= 64) f(std::integral_constant<int, 1>{});
+  else if (E <= 128) f(std::integral_constant<int, 2>{});
+  else if (E <= 256) f(std::integral_constant<int, 4>{});
+  else if (E <= 512) f(std::integral_constant<int, 8>{});
+  else f(std::integral_constant<int, 16>{});
+}
+
+__device__ __forceinline__ PassInfo fused_pass(const FusedArgs& f, const TierMask& tm, int p,
+                                               const BlockRoute& br) {
+  const int e = __builtin_amdgcn_readfirstlane(br.ids[p]);
+  const int code = tier_code(tm, e);
+  PassInfo pi;
+  pi.slot = p;
+  pi.token = p / f.k;
+  pi.nf3 = (code >> 16) != 0;
+  pi.loc = code & 0xFFFF;
+  pi.ok = (unsigned)e < (unsigned)f.E && pi.loc < (pi.nf3 ? f.a13.E3 : f.a13.E4);
+  return pi;
+}
+
+// this wave's run [b, e) of a flat range of n chunks: runs numbered block-major (the
+// waves of a block take consecutive runs) or wave-major (consecutive blocks do)
+template <bool WAVE_MAJOR>
+__device__ __forceinline__ void wave_run(const FusedArgs& f, int n, int* b, int* e) {
+  const int wv = threadIdx.x >> 6;
+  const int gw = WAVE_MAJOR ? wv * f.nwork_blocks + (int)blockIdx.x : (int)blockIdx.x * kGemvWaves + wv;
+  *b = (int)((long)gw * n / f.nwork);
+  *e = (int)((long)(gw + 1) * n / f.nwork);
+}
+
+// waits until all W13 chunks of slot p are done (bounded), polling this block's copy of
+// the slot's ready flag
+__device__ __forceinline__ void wait_h(const FusedArgs& f, int p) {
+  const uint32_t* c =
+      f.sync + f.ready_base + (p * kReadyCopies + (int)(blockIdx.x % kReadyCopies)) * kSyncLine;
+  for (int it = 0;; ++it) {
+    if (sync_load(c) != 0u) break;
+    if (it == kSpinLimit) {
+      if ((threadIdx.x & (kWave - 1)) == 0) sync_add(f.sync + kSyncTimeouts, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
+// y[t, 64 g + lane] = sum_j w[t, j] * o[t*k + j, 64 g + lane] in fixed j order (the
+// order of decode_combine_kernel), eight slot rows requested at a time
+__device__ __forceinline__ void fused_combine(const FusedArgs& f, int t, int g, const BlockRoute& br) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int H = f.a2.rows;
+  const int n = g * kCombRows + lane;
+  float acc = 0.0f;
+#pragma unroll
+  for (int j0 = 0; j0 < kMaxTopK; j0 += 8) {
+    float ov[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ov[j] = j0 + j < f.k ? load_coherent(f.o + (size_t)(t * f.k + j0 + j) * H + n) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc = __builtin_fmaf(j0 + j < f.k ? br.w[t * f.k + j0 + j] : 0.0f, ov[j], acc);
+  }
+  f.y[(size_t)t * H + n] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
+}
+
+template <int LR13, int KU13, int RI13, int LR2, int KU2, int RI2>
+__global__ __launch_bounds__(kGemvThreads) void decode_fused_kernel(FusedArgs f, TierMask tm) {
+  constexpr int CH13 = (kWave / LR13) * RI13;
+  constexpr int CH2 = (kWave / LR2) * RI2;
+  constexpr int KD2 = 16 * LR2 * KU2;          // dwords of one staged h row
+  static_assert(kCombRows % CH2 == 0, "combine groups hold whole W2 chunks");
+  struct Luts {
+    uint32_t w13[64 * kWave];   // [pair field][lane]: bf16 pairs of scaled NF3 levels
+    uint32_t w2[64 * kWave];    // the same in fp16
+  };
+  union Big {
+    Luts luts;
+    GroupSmem group;
+  };
+  __shared__ Big big;
+  __shared__ BlockRoute br;
+  __shared__ int last_block;
+  extern __shared__ uint32_t h_stage[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+
+  if (blockIdx.x == gridDim.x - 1) {
+    // inspection outputs: routing of every token, pass records, tier map, grouping
+    for (int t = wv; t < f.M; t += kGemvWaves) {
+      float wl;
+      const int e = route_select_any(f.logits + (size_t)t * f.E, f.E, f.k, lane, &wl);
+      if (lane < f.k) {
+        const int s = t * f.k + lane;
+        f.ids[s] = e;
+        f.w[s] = wl;
+        reinterpret_cast<int4*>(f.pass)[s] = make_int4(s, tier_code(tm, e), t, e);
+      }
+    }
+    for (int e = threadIdx.x; e < f.E; e += kGemvThreads) f.expert_tier[e] = tier_code(tm, e);
+    __syncthreads();
+    decode_grouping(f.ga, tm, big.group);
+  } else {
+    // every token's routing (wave w: tokens w and w + 4), its logits rows requested
+    // before the level tables are built
+    with_nv(f.E, [&](auto nvc) {
+      constexpr int NV = decltype(nvc)::value;
+      float xa[NV], xb[NV];
+      const int ta = wv, tb = wv + kGemvWaves;
+      if (ta < f.M) route_fetch<NV>(f.logits + (size_t)ta * f.E, f.E, lane, xa);
+      if (tb < f.M) route_fetch<NV>(f.logits + (size_t)tb * f.E, f.E, lane, xb);
+      build_nf3_lut<false>(big.luts.w13, kNF3TableScaleBf16);
+      build_nf3_lut<true>(big.luts.w2, kNF3TableScaleF16);
+      float wl;
+      if (ta < f.M) {
+        const int e = route_rank<NV>(xa, f.E, f.k, lane, &wl);
+        if (lane < f.k) {
+          br.ids[ta * f.k + lane] = e;
+          br.w[ta * f.k + lane] = wl;
+        }
+      }
+      if (tb < f.M) {
+        const int e = route_rank<NV>(xb, f.E, f.k, lane, &wl);
+        if (lane < f.k) {
+          br.ids[tb * f.k + lane] = e;
+          br.w[tb * f.k + lane] = wl;
+        }
+      }
+    });
+    __syncthreads();
+    const uint32_t* lut13 = big.luts.w13 + lane;
+    const uint32_t* lut2 = big.luts.w2 + lane;
+    const int npass = f.M * f.k;
+
+    // ---- W13 + SwiGLU: run gw of the flat range (blocks first)
+    {
+      int b, e;
+      wave_run<false>(f, npass * f.per13, &b, &e);
+      W13Buf<KU13, RI13> A, B;
+      for (int ch = b; ch < e;) {
+        const int p = __builtin_amdgcn_readfirstlane(ch / f.per13);
+        const int p_end = min(e, (p + 1) * f.per13);
+        const PassInfo pi = fused_pass(f, tm, p, br);
+        if (pi.ok) {
+          const float g = pi.nf3 ? 1.0f / kNF3TableScaleBf16
+                                 : (f.a13.kept_fmt == HMOE_KEPT_NVFP4 ? f.a13.kg[pi.loc] : 1.0f);
+          with_format(f.a13, pi, [&](auto fm) {
+            w13_pass<LR13, KU13, RI13, decltype(fm)::value, true>(f.a13, pi, ch, p_end, p * f.per13, g,
+                                                                  lut13, A, B, false);
+          });
+        }
+        wait_vmem();
+        const uint32_t inc = (uint32_t)(p_end - ch);
+        uint32_t old = 0;
+        if (lane == 0) old = sync_add(f.sync + kSyncH + p * kSyncLine, inc);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old + inc == (uint32_t)f.per13 && lane < kReadyCopies)
+          sync_store(f.sync + f.ready_base + (p * kReadyCopies + lane) * kSyncLine, 1u);
+        ch = p_end;
+      }
+    }
+
+    // ---- W2 and the combine: run gw of the flat range (waves first)
+    {
+      int b, e;
+      wave_run<true>(f, npass * f.per2, &b, &e);
+      uint32_t* hs = h_stage + KD2 * wv;
+      constexpr int CPG = kCombRows / CH2;   // W2 chunks per combine group
+      W2Buf<KU2, RI2> A, B;
+      for (int ch = b; ch < e;) {
+        const int p = __builtin_amdgcn_readfirstlane(ch / f.per2);
+        const int p_end = min(e, (p + 1) * f.per2);
+        const int t = p / f.k;
+        const PassInfo pi = fused_pass(f, tm, p, br);
+        // the first chunk's weights are requested before the wait for h
+        if (pi.ok)
+          with_format(f.a2, pi, [&](auto fm) {
+            w2_load<LR2, KU2, RI2, decltype(fm)::value>(f.a2, pi.loc, (ch - p * f.per2) * CH2, A);
+          });
+        wait_h(f, p);
+        if (pi.ok) {
+          const float gt = pi.nf3 ? 1.0f / kNF3TableScaleF16
+                                  : (f.a2.kept_fmt == HMOE_KEPT_NVFP4 ? f.a2.kg[pi.loc] : 1.0f);
+          with_format(f.a2, pi, [&](auto fm) {
+            w2_pass<LR2, KU2, RI2, decltype(fm)::value, true>(f.a2, pi, ch, p_end, p * f.per2, gt, lut2,
+                                                              hs, A, B, true);
+          });
+        }
+        wait_vmem();
+        for (int c = ch; c < p_end;) {
+          const int grp = (c - p * f.per2) / CPG;
+          const int gend = min(p_end, p * f.per2 + (grp + 1) * CPG);
+          const uint32_t inc = (uint32_t)(gend - c);
+          uint32_t old = 0;
+          if (lane == 0) old = sync_add(f.sync + f.comb_base + (t * f.G + grp) * kSyncLine, inc);
+          old = __builtin_amdgcn_readfirstlane(old);
+          if (old + inc == (uint32_t)(f.k * CPG)) fused_combine(f, t, grp, br);
+          c = gend;
+        }
+        ch = p_end;
+      }
+    }
+  }
+
+  // ---- exit: the last block clears the counters for the next launch
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) last_block = sync_add(f.sync + kSyncExit, 1u) + 1u == gridDim.x;
+  __syncthreads();
+  if (last_block) {
+    const int nh = f.M * f.k, nc = f.M * f.G;
+    for (int i = threadIdx.x; i < nh; i += kGemvThreads) sync_store(f.sync + kSyncH + i * kSyncLine, 0u);
+    for (int i = threadIdx.x; i < nh * kReadyCopies; i += kGemvThreads)
+      sync_store(f.sync + f.ready_base + i * kSyncLine, 0u);
+    for (int i = threadIdx.x; i < nc; i += kGemvThreads) sync_store(f.sync + f.comb_base + i * kSyncLine, 0u);
+    if (threadIdx.x == 0) sync_store(f.sync + kSyncExit, 0u);
+  }
+}
+
+// zero-fills n words of the sync region (moe_scratch_init; no memset, so it is safe
+// under graph capture)
+__global__ __launch_bounds__(256) void sync_clear_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
@@ -856,9 +1201,9 @@ static int cu_count() {
   return cached;
 }
 
-hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
-                         uint16_t* y, void* scratch, int stage, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
+// GEMV arguments of one decode stage (W13 or W2) over the scratch regions
+static GemvArgs gemv_args(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
+                          void* scratch, bool w13) {
   char* base = static_cast<char*>(scratch);
   const ScratchPlan& P = L.plan;
   GemvArgs a{};
@@ -872,6 +1217,45 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
   a.I = L.I;
   float* h = reinterpret_cast<float*>(base + P.h_dec);
   float* o = reinterpret_cast<float*>(base + P.o_dec);
+  if (w13) {
+    a.kq = W.kept_w13_q; a.ks = W.kept_w13_s; a.kg = W.kept_w13_g;
+    a.nq = W.nf3_w13_q; a.ns = W.nf3_w13_s;
+    a.rows = 2 * L.I; a.K = L.H; a.out_units = L.I;
+    a.act_bf16 = x;
+    a.h_out = h;
+  } else {
+    a.kq = W.kept_w2_q; a.ks = W.kept_w2_s; a.kg = W.kept_w2_g;
+    a.nq = W.nf3_w2_q; a.ns = W.nf3_w2_s;
+    a.rows = L.H; a.K = L.I; a.out_units = L.H;
+    a.act_f32 = h;
+    a.o_out = o;
+  }
+  return a;
+}
+
+static GroupArgs group_args(const Layer& L, int M, void* scratch) {
+  char* base = static_cast<char*>(scratch);
+  const ScratchPlan& P = L.plan;
+  GroupArgs ga;
+  ga.ids = reinterpret_cast<const int32_t*>(base + P.topk_ids);
+  ga.M = M;
+  ga.E = L.E;
+  ga.k = L.k;
+  ga.E4 = L.E4;
+  ga.counts = reinterpret_cast<int32_t*>(base + P.d_counts);
+  ga.experts = reinterpret_cast<int32_t*>(base + P.d_experts);
+  ga.nslots = reinterpret_cast<int32_t*>(base + P.d_nslots);
+  ga.slots = reinterpret_cast<int32_t*>(base + P.d_slots);
+  return ga;
+}
+
+hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
+                         uint16_t* y, void* scratch, int stage, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  char* base = static_cast<char*>(scratch);
+  const ScratchPlan& P = L.plan;
+  const GemvArgs a = gemv_args(L, W, x, M, scratch, true);
+  float* o = reinterpret_cast<float*>(base + P.o_dec);
   // a persistent grid: as many blocks as fit on the GPU at once, never more waves
   // than chunks
   auto grid_for = [&](GemvFn fn, const GemvTiling& t, int out_units, size_t smem) {
@@ -881,24 +1265,14 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
     return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
   };
   if (stage == HMOE_STAGE_W13) {
-    GemvArgs b = a;
-    b.kq = W.kept_w13_q; b.ks = W.kept_w13_s; b.kg = W.kept_w13_g;
-    b.nq = W.nf3_w13_q; b.ns = W.nf3_w13_s;
-    b.rows = 2 * L.I; b.K = L.H; b.out_units = L.I;
-    b.act_bf16 = x;
-    b.h_out = h;
+    const GemvArgs b = a;
     GemvFn fn = pick_gemv<true>(L.w13);
     if (!fn) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fn, dim3(grid_for(fn, L.w13, L.I, 0)), dim3(kGemvThreads), 0, s, b);
     return hipGetLastError();
   }
   if (stage == HMOE_STAGE_W2) {
-    GemvArgs b = a;
-    b.kq = W.kept_w2_q; b.ks = W.kept_w2_s; b.kg = W.kept_w2_g;
-    b.nq = W.nf3_w2_q; b.ns = W.nf3_w2_s;
-    b.rows = L.H; b.K = L.I; b.out_units = L.H;
-    b.act_f32 = h;
-    b.o_out = o;
+    const GemvArgs b = gemv_args(L, W, x, M, scratch, false);
     GemvFn fn = pick_gemv<false>(L.w2);
     if (!fn) return hipErrorInvalidValue;
     const size_t smem = (size_t)kGemvWaves * L.I * 2;  // one fp16 h row per wave
@@ -907,16 +1281,7 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
   }
   if (stage == HMOE_STAGE_COMBINE) {
     const int n = M * L.H;
-    GroupArgs ga;
-    ga.ids = reinterpret_cast<const int32_t*>(base + P.topk_ids);
-    ga.M = M;
-    ga.E = L.E;
-    ga.k = L.k;
-    ga.E4 = L.E4;
-    ga.counts = reinterpret_cast<int32_t*>(base + P.d_counts);
-    ga.experts = reinterpret_cast<int32_t*>(base + P.d_experts);
-    ga.nslots = reinterpret_cast<int32_t*>(base + P.d_nslots);
-    ga.slots = reinterpret_cast<int32_t*>(base + P.d_slots);
+    const GroupArgs ga = group_args(L, M, scratch);
     // one more block than the sum needs: it builds the grouping
     hipLaunchKernelGGL(decode_combine_kernel, dim3((n + 255) / 256 + 1), dim3(256), 0, s, o,
                        reinterpret_cast<const float*>(base + P.topk_w), M, L.k, L.H, y, ga,
@@ -924,6 +1289,106 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
+}
+
+// ---- single-launch decode: the tiling pairs (W13 over K = H, W2 over K = I) it is
+// instantiated for; other layer shapes run the four-launch path
+typedef void (*FusedFn)(FusedArgs, TierMask);
+
+static FusedFn pick_fused(const GemvTiling& a, const GemvTiling& b) {
+#define HMOE_FUSED_CASE(L1, K1, R1, L2, K2, R2)                                        \
+  if (a.lr == L1 && a.ku == K1 && a.ri == R1 && b.lr == L2 && b.ku == K2 && b.ri == R2) \
+    return decode_fused_kernel<L1, K1, R1, L2, K2, R2>;
+  HMOE_FUSED_CASE(8, 1, 2, 4, 1, 2)     // H = 256, I = 128
+  HMOE_FUSED_CASE(4, 3, 1, 8, 1, 2)     // H = 384, I = 256
+  HMOE_FUSED_CASE(16, 1, 2, 8, 1, 2)    // H = 512, I = 256
+  HMOE_FUSED_CASE(32, 1, 2, 16, 1, 2)   // H = 1024, I = 512
+  HMOE_FUSED_CASE(64, 1, 2, 8, 3, 1)    // H = 2048, I = 768 (Qwen3-MoE-shaped)
+  HMOE_FUSED_CASE(64, 3, 1, 64, 1, 2)   // H = 6144, I = 2048 (GLM-class)
+  HMOE_FUSED_CASE(64, 2, 2, 32, 3, 1)   // H = 4096, I = 1536
+  HMOE_FUSED_CASE(64, 2, 2, 64, 1, 2)   // H = 4096, I = 2048
+  HMOE_FUSED_CASE(64, 1, 2, 16, 3, 1)   // H = 2048, I = 1536
+#undef HMOE_FUSED_CASE
+  return nullptr;
+}
+
+bool fused_decode_available(const Layer& L) { return pick_fused(L.w13, L.w2) != nullptr; }
+
+// words of the single-launch decode's sync region: exit, timeouts, h_cnt per slot
+// (8k slots), kReadyCopies ready flags per slot, comb per token and 64-row group (8
+// tokens), one 64-byte line each
+size_t fused_sync_words(int k, int H) {
+  return (size_t)(2 + kDecodeMaxM * k * (1 + kReadyCopies) + kDecodeMaxM * (H / kCombRows)) *
+         kSyncLine;
+}
+
+static int fused_resident_blocks(FusedFn fn, size_t smem) {
+  static FusedFn cfn[8] = {};
+  static size_t csmem[8] = {};
+  static int cn[8] = {};
+  for (int i = 0; i < 8; ++i) {
+    if (cfn[i] == fn && csmem[i] == smem) return cn[i];
+    if (cfn[i] == nullptr) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
+                                                       kGemvThreads, smem) != hipSuccess || n < 1)
+        n = 1;
+      cfn[i] = fn;
+      csmem[i] = smem;
+      cn[i] = n;
+      return n;
+    }
+  }
+  return 1;
+}
+
+hipError_t launch_decode_fused(const Layer& L, const hmoe_weights& W, const uint16_t* x,
+                               const float* logits, int M, uint16_t* y, void* scratch,
+                               hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  FusedFn fn = pick_fused(L.w13, L.w2);
+  if (!fn) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(scratch);
+  const ScratchPlan& P = L.plan;
+  FusedArgs f{};
+  f.a13 = gemv_args(L, W, x, M, scratch, true);
+  f.a2 = gemv_args(L, W, x, M, scratch, false);
+  f.logits = logits;
+  f.M = M;
+  f.E = L.E;
+  f.k = L.k;
+  f.per13 = L.I / ((64 / L.w13.lr) * L.w13.ri);
+  f.per2 = L.H / ((64 / L.w2.lr) * L.w2.ri);
+  f.G = L.H / kCombRows;
+  f.ready_base = kSyncH + kDecodeMaxM * L.k * kSyncLine;
+  f.comb_base = f.ready_base + kDecodeMaxM * L.k * kReadyCopies * kSyncLine;
+  f.sync = reinterpret_cast<uint32_t*>(base + P.d_sync);
+  f.o = f.a2.o_out;
+  f.y = y;
+  f.ids = reinterpret_cast<int32_t*>(base + P.topk_ids);
+  f.w = reinterpret_cast<float*>(base + P.topk_w);
+  f.expert_tier = reinterpret_cast<int32_t*>(base + P.expert_tier);
+  f.pass = reinterpret_cast<int32_t*>(base + P.d_pass);
+  f.ga = group_args(L, M, scratch);
+  // a persistent grid that is resident at once: the work blocks, never more waves than
+  // W13 chunks, plus the block that writes the inspection outputs
+  const size_t smem = (size_t)kGemvWaves * L.I * 2;   // one fp16 h row per wave
+  const long cap = (long)fused_resident_blocks(fn, smem) * cu_count() - 1;
+  const long n13 = (long)M * L.k * f.per13;
+  long work = (n13 + kGemvWaves - 1) / kGemvWaves;
+  if (work > cap) work = cap;
+  if (work < 1) work = 1;
+  f.nwork_blocks = (int)work;
+  f.nwork = (int)work * kGemvWaves;
+  hipLaunchKernelGGL(fn, dim3((unsigned)work + 1), dim3(kGemvThreads), smem, s, f, make_tier_mask(L));
+  return hipGetLastError();
+}
+
+hipError_t launch_sync_clear(const Layer& L, void* scratch, hipStream_t s) {
+  const int n = (int)fused_sync_words(L.k, L.H);
+  uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<char*>(scratch) + L.plan.d_sync);
+  hipLaunchKernelGGL(sync_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
 }
 
 }  // namespace hmoe

@@ -25,6 +25,7 @@ struct ScratchPlan {
   size_t topk_ids = 0, topk_w = 0, expert_tier = 0;
   size_t d_counts = 0, d_experts = 0, d_nslots = 0, d_slots = 0, d_pass = 0;
   size_t h_dec = 0, o_dec = 0;
+  size_t d_sync = 0;                       // single-launch decode counters (zero between calls)
   size_t a_counts = 0;                     // int32 [E] slot counts per expert
   size_t a_slots[2] = {0, 0}, a_bexp[2] = {0, 0}, a_eoff[2] = {0, 0}, a_npad[2] = {0, 0};
   size_t h_pre = 0, o_pre = 0, x16_pre = 0, xe_pre = 0;
@@ -48,6 +49,8 @@ struct Layer {
   int max_distinct = 0;                        // min(8k, E)
   int cap[2] = {0, 0};                         // align capacity per tier
   GemvTiling w13, w2;
+  bool fused_decode = false;                   // the forward runs decode as one launch
+  bool single_available = false;               // a single-launch decode exists for H, I
   ScratchPlan plan;
 };
 
@@ -70,6 +73,15 @@ hipError_t launch_align(const Layer& L, const int32_t* ids, int M, void* scratch
 // decode.hip: one stage (HMOE_STAGE_W13 / _W2 / _COMBINE) of the decode path
 hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
                          uint16_t* y, void* scratch, int stage, hipStream_t s);
+
+// decode.hip: the whole decode forward in one launch (only for the layer shapes
+// fused_decode_available accepts), the size of its sync region, and its zero fill
+bool fused_decode_available(const Layer& L);
+size_t fused_sync_words(int k, int H);
+hipError_t launch_decode_fused(const Layer& L, const hmoe_weights& W, const uint16_t* x,
+                               const float* logits, int M, uint16_t* y, void* scratch,
+                               hipStream_t s);
+hipError_t launch_sync_clear(const Layer& L, void* scratch, hipStream_t s);
 
 // prefill.hip: one stage (HMOE_STAGE_W13 / _W2 / _COMBINE) of the prefill path
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,

@@ -60,6 +60,7 @@ void plan_scratch(hmoe::Layer& L) {
   P.d_pass = take(dec_slots * hmoe::kPassRec * 4);
   P.h_dec = take(dec_slots * L.I * 4);
   P.o_dec = take(dec_slots * L.H * 4);
+  P.d_sync = take(hmoe::fused_sync_words(L.k, L.H) * 4);
   for (int t = 0; t < 2; ++t) {
     const int cap = L.cap[t];
     const int ne = t == 0 ? L.E4 : L.E3;
@@ -147,6 +148,8 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
     return fail(HMOE_ERR_INVALID_ARG, "unknown kept_format");
   if (d->block_m != 0 && d->block_m != 16 && d->block_m != 32 && d->block_m != 64 && d->block_m != 128)
     return fail(HMOE_ERR_INVALID_ARG, "block_m must be 0, 16, 32, 64 or 128");
+  if (d->decode_launch != HMOE_DECODE_STAGED && d->decode_launch != HMOE_DECODE_SINGLE_LAUNCH)
+    return fail(HMOE_ERR_INVALID_ARG, "unknown decode_launch");
   if (d->num_experts > hmoe::kMaxExperts) return fail(HMOE_ERR_UNSUPPORTED, "num_experts > 1024");
   if (d->top_k > hmoe::kMaxTopK) return fail(HMOE_ERR_UNSUPPORTED, "top_k > 16");
   if (d->hidden % 128 || d->inter % 128)
@@ -203,6 +206,13 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
     return fail(HMOE_ERR_UNSUPPORTED, "no decode GEMV tiling for H=" + std::to_string(d->hidden) +
                                           ", I=" + std::to_string(d->inter));
   }
+  L.single_available = hmoe::fused_decode_available(L);
+  if (d->decode_launch == HMOE_DECODE_SINGLE_LAUNCH && !L.single_available) {
+    delete h;
+    return fail(HMOE_ERR_UNSUPPORTED, "no single-launch decode for H=" + std::to_string(d->hidden) +
+                                          ", I=" + std::to_string(d->inter));
+  }
+  L.fused_decode = d->decode_launch == HMOE_DECODE_SINGLE_LAUNCH;
   plan_scratch(L);
   *out = h;
   return HMOE_OK;
@@ -226,6 +236,8 @@ hmoe_status moe_layer_query(const hmoe_layer* layer, hmoe_layer_info* out) {
   out->max_distinct = L.max_distinct;
   out->cap_kept = L.cap[0];
   out->cap_nf3 = L.cap[1];
+  out->fused_decode = L.fused_decode ? 1 : 0;
+  out->single_launch_available = L.single_available ? 1 : 0;
   return HMOE_OK;
 }
 
@@ -293,6 +305,7 @@ hmoe_status moe_decode_view(const hmoe_layer* layer, void* scratch, hmoe_decode_
   out->expert_tier = reinterpret_cast<int32_t*>(b + L.plan.expert_tier);
   out->passes = reinterpret_cast<int32_t*>(b + L.plan.d_pass);
   out->max_distinct = L.max_distinct;
+  out->sync_timeouts = reinterpret_cast<int32_t*>(b + L.plan.d_sync) + 16;
   return HMOE_OK;
 }
 
@@ -346,6 +359,18 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
                                const uint16_t* x, const float* router_logits, int32_t M,
                                uint16_t* y, void* scratch, size_t scratch_bytes,
                                hipStream_t stream) {
+  if (layer && layer->L.fused_decode && M > 0 && M <= hmoe::kDecodeMaxM) {
+    const hmoe::Layer& L = layer->L;
+    if (M > L.max_tokens) return fail(HMOE_ERR_CAPACITY, "M exceeds max_tokens");
+    if (hmoe_status st = check_weights(L, weights)) return st;
+    if (hmoe_status st = check_scratch(L, scratch, scratch_bytes)) return st;
+    if (!x || !router_logits || !y || !aligned(x, 16) || !aligned(router_logits, 16) ||
+        !aligned(y, 16))
+      return fail(HMOE_ERR_ALIGN, "x, router_logits and y must be non-NULL and 16-byte aligned");
+    hipError_t err = hmoe::launch_decode_fused(L, *weights, x, router_logits, M, y, scratch, stream);
+    if (err != hipSuccess) return hip_fail(err, "decode launch");
+    return HMOE_OK;
+  }
   for (int32_t stage = HMOE_STAGE_ROUTE; stage <= HMOE_STAGE_COMBINE; ++stage) {
     const hmoe_status st = hybrid_moe_forward_stage(layer, weights, x, router_logits, M, y, scratch,
                                                     scratch_bytes, stage, stream);
@@ -367,6 +392,15 @@ hmoe_status hybrid_moe_forward_static(const hmoe_layer* layer, const hmoe_weight
   hipError_t err = hmoe::static_scratch(&scratch);
   if (err != hipSuccess) return hip_fail(err, "static scratch address");
   return hybrid_moe_forward(layer, weights, x, router_logits, M, y, scratch, have, stream);
+}
+
+hmoe_status moe_scratch_init(const hmoe_layer* layer, void* scratch, size_t scratch_bytes,
+                             hipStream_t stream) {
+  if (hmoe_status st = check_layer(layer)) return st;
+  if (hmoe_status st = check_scratch(layer->L, scratch, scratch_bytes)) return st;
+  hipError_t err = hmoe::launch_sync_clear(layer->L, scratch, stream);
+  if (err != hipSuccess) return hip_fail(err, "scratch init launch");
+  return HMOE_OK;
 }
 
 hmoe_status moe_dequant(const hmoe_layer* layer, const hmoe_weights* weights, int32_t expert,
