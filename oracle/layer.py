@@ -12,6 +12,11 @@ Pages (cited by title and section):
 * PR #104 description: bit map values 4 = kept tier, 3 = NF3; the kept format
   may switch the kept tier to MXFP4; expert weights are demultiplexed into
   compact tier-local storage.
+* vllm-project/vllm PR #42428 "W4A16 NVFP4 fused MoE", "What's in this PR": the
+  W4A16 path sits beside W4A4 backends, whose activations are 4-bit as well. The
+  W4A4 variant here (act_format "mxfp4") applies to an MXFP4 kept tier: each
+  kept-tier matmul input (x before W13, h before W2) is rounded to MXFP4 along K,
+  blocks of 32, by the OCP MX v1.0 conversion the weight quantiser uses.
 Routing (softmax over the router logits, top-k, renormalised) and SwiGLU
 experts are the layer's definition where the pages do not spell them out.
 """
@@ -155,15 +160,43 @@ def expert_mlp(x: np.ndarray, w13: np.ndarray, w2: np.ndarray):
     return h, h @ w2.astype(np.float64).T
 
 
-def forward(layer: dict, x_bits: np.ndarray, logits: np.ndarray, tokens=None, threads: int = 1):
+def mxfp4_activation(a: np.ndarray) -> np.ndarray:
+    """Activations rounded to MXFP4 along their last axis (blocks of 32, the OCP MX
+    v1.0 conversion of formats.mxfp4_quantize) and decoded back: the fp32 values a
+    W4A4 matmul multiplies."""
+    a = np.asarray(a, dtype=np.float32)
+    q, s = F.mxfp4_quantize(a.reshape(-1, a.shape[-1]))
+    return F.mxfp4_dequant(q, s).reshape(a.shape)
+
+
+def expert_mlp_w4a4(x: np.ndarray, w13: np.ndarray, w2: np.ndarray):
+    """SwiGLU expert with 4-bit activations: x is rounded to MXFP4 before W13; h =
+    silu(a) * b is rounded to fp32 (the width it is computed in) and then to MXFP4
+    before W2. Products and sums in fp64. Returns (the MXFP4 h that W2 sees, o)."""
+    I = w2.shape[1]
+    xq = mxfp4_activation(x).astype(np.float64)
+    z = xq @ w13.astype(np.float64).T
+    h = silu(z[:, :I]) * z[:, I:]
+    hq = mxfp4_activation(h.astype(np.float32)).astype(np.float64)
+    return hq, hq @ w2.astype(np.float64).T
+
+
+def forward(layer: dict, x_bits: np.ndarray, logits: np.ndarray, tokens=None, threads: int = 1,
+            act_format: str = "bf16"):
     """The layer: route once, run every selected (token, expert) pair through
     the expert's MLP in its own tier, and add the outputs into one top-k
     weighted sum y[t] = sum_j w[t, j] * o[t, j]. `tokens` restricts the
     returned rows to a subset (the routing result is still for every token).
     `threads` > 1 dequantises and runs several experts at once; the outputs are
     still added into y one expert at a time in ascending expert id, so the result
-    does not depend on it. Returns ids, weights, per-slot h (only for the computed
-    tokens) and y (fp64, one row per computed token)."""
+    does not depend on it. act_format "mxfp4" runs the kept tier as W4A4
+    (expert_mlp_w4a4; the layer's kept tier must be MXFP4), "bf16" (default) every
+    expert as W4A16. Returns ids, weights, per-slot h (only for the computed tokens)
+    and y (fp64, one row per computed token)."""
+    if act_format not in ("bf16", "mxfp4"):
+        raise ValueError("act_format must be 'bf16' or 'mxfp4'")
+    if act_format == "mxfp4" and kept_format_of(layer) != "mxfp4":
+        raise ValueError("W4A4 needs an MXFP4 kept tier")
     E, k = layer["E"], layer["top_k"]
     ids, w = route(logits, k)
     M = ids.shape[0]
@@ -175,10 +208,15 @@ def forward(layer: dict, x_bits: np.ndarray, logits: np.ndarray, tokens=None, th
     sel = ids[tokens]
     experts = sorted(set(int(v) for v in sel.reshape(-1)))
 
+    tier, _ = tier_map(layer["bit_map"], E)
+
     def run(e):
         rows, cols = np.nonzero(sel == e)
         w13, w2 = expert_weights(layer, e)
-        h, o = expert_mlp(x[rows], w13, w2)
+        if act_format == "mxfp4" and tier[e] == KEPT:
+            h, o = expert_mlp_w4a4(x[rows], w13, w2)
+        else:
+            h, o = expert_mlp(x[rows], w13, w2)
         return rows, cols, h, o
 
     def add(result):

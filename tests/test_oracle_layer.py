@@ -259,3 +259,109 @@ def test_demux_places_each_expert_by_brute_force():
     back = L.checkpoint_experts(layer)
     for e in range(E):
         assert set(back[e]) == set(mine[e]) and all(np.array_equal(back[e][k], mine[e][k]) for k in mine[e])
+
+
+# ---------------------------------------------------------------- W4A4 (MXFP4 activations)
+
+_E2M1_MAGS = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _mx_round_block(vals):
+    """One 32-block by the OCP MX v1.0 conversion, written out: shared exponent
+    floor(log2(amax)) - 2 (from math.frexp), clamped to [-127, 127]; each element
+    divided by 2^shared and set to the nearest E2M1 magnitude (ties to the one with an
+    even code index, |t| clipped to 6), sign kept."""
+    import math
+    amax = max(abs(float(v)) for v in vals)
+    if amax == 0.0:
+        return [0.0] * len(vals)
+    shared = min(max(math.frexp(amax)[1] - 1 - 2, -127), 127)
+    out = []
+    for v in vals:
+        t = math.ldexp(float(v), -shared)
+        a = min(abs(t), 6.0)
+        best = 0
+        for i in range(1, 8):
+            d, db = abs(a - _E2M1_MAGS[i]), abs(a - _E2M1_MAGS[best])
+            if d < db or (d == db and i % 2 == 0 and best % 2 == 1):
+                best = i
+        out.append(math.copysign(math.ldexp(_E2M1_MAGS[best], shared), t) if best else 0.0)
+    return out
+
+
+def test_mxfp4_activation_brute_force():
+    rng = np.random.default_rng(31)
+    a = (rng.standard_normal((6, 128)) * np.exp(rng.standard_normal((6, 1)) * 3)).astype(np.float32)
+    a[0, :32] = 0.0                                        # an all-zero block
+    a[1, :32] = np.float32(2.0 ** -130)                    # subnormal block: exponent clamp
+    a[2, :8] = np.array([4, 1, 0.5, 0.25, 0.75, 1.25, 1.75, 2.5], np.float32)   # ties
+    a[2, 8:16] = np.array([3.5, 5, -0.25, -0.75, 6.5, -7, 0.125, 3], np.float32)
+    got = L.mxfp4_activation(a)
+    ref = np.array([sum((_mx_round_block(row[b:b + 32]) for b in range(0, 128, 32)), [])
+                    for row in a.astype(np.float64)], dtype=np.float64)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_w4a4_layer_brute_force_loops():
+    """The W4A4 forward (MXFP4 kept tier, MXFP4 activations) against explicit loops:
+    per-block rounding of x and of h (after fp32 rounding) by the written-out OCP
+    conversion, dot products element by element."""
+    bm = np.array([4, 4, 4, 4, 3, 3, 3, 3], np.uint8)
+    lay, w = _tiny_layer(bm, "mxfp4")
+    x = synth.activations_bf16(w, 2)
+    lg = synth.router_logits(w, 2)
+    lg[0, 1] += 9.0     # token 0 takes a kept-tier expert first
+    out = L.forward(lay, x, lg, act_format="mxfp4")
+    xs = F.bf16_value(x).astype(np.float64)
+    tier, _ = L.tier_map(bm, 8)
+    for t in range(2):
+        order = sorted(range(8), key=lambda e: (-float(lg[t, e]), e))[:2]
+        ex = [np.exp(float(lg[t, e]) - float(lg[t, order[0]])) for e in order]
+        y = np.zeros(256)
+        for j, e in enumerate(order):
+            w13, w2 = L.expert_weights(lay, e)
+            kept = tier[e] == L.KEPT
+            xv = sum((_mx_round_block(xs[t][b:b + 32]) for b in range(0, 256, 32)), []) if kept else list(xs[t])
+            h = np.zeros(128)
+            for i in range(128):
+                a = sum(float(w13[i][c]) * xv[c] for c in range(256))
+                b = sum(float(w13[128 + i][c]) * xv[c] for c in range(256))
+                h[i] = a / (1.0 + np.exp(-a)) * b
+            if kept:
+                h32 = h.astype(np.float32).astype(np.float64)
+                h = np.array(sum((_mx_round_block(h32[b:b + 32]) for b in range(0, 128, 32)), []))
+            for n in range(256):
+                y[n] += ex[j] / sum(ex) * float(np.dot(w2[n].astype(np.float64), h))
+        assert np.allclose(out["y"][t], y, rtol=1e-9, atol=1e-12), t
+    assert any(tier[e] == L.KEPT for e in out["ids"].ravel())
+
+
+def test_w4a4_leaves_the_nf3_tier_and_equals_w4a16_there():
+    bm = np.array([4, 4, 4, 4, 3, 3, 3, 3], np.uint8)
+    lay, w = _tiny_layer(bm, "mxfp4")
+    x = synth.activations_bf16(w, 6)
+    lg = synth.router_logits(w, 6)
+    lg[:, :4] -= 50.0   # every token routed to NF3 experts only
+    a = L.forward(lay, x, lg, act_format="mxfp4")
+    b = L.forward(lay, x, lg)
+    assert np.array_equal(a["y"], b["y"])
+
+
+def test_w4a4_on_representable_x_matches_w4a16_before_w2():
+    """With x exactly representable in MXFP4 the W13 input is unchanged, so W4A4 and
+    W4A16 differ only by h's rounding: the W4A4 h equals the MXFP4 rounding of the
+    W4A16 h (rounded to fp32 first)."""
+    bm = np.array([4, 4, 4, 4, 3, 3, 3, 3], np.uint8)
+    lay, w = _tiny_layer(bm, "mxfp4")
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, (3, 256)).astype(np.uint8)
+    scales = rng.integers(124, 130, (3, 256 // 32)).astype(np.uint8)
+    xv = F.mxfp4_dequant(F.pack_fp4(codes), scales)
+    x = F.bf16_bits(xv)
+    assert np.array_equal(F.bf16_value(x), xv)          # bf16 holds the MX values exactly
+    lg = synth.router_logits(w, 3)
+    lg[:, 4:] -= 50.0   # kept-tier experts only
+    a = L.forward(lay, x, lg, act_format="mxfp4")
+    b = L.forward(lay, x, lg)
+    for s, h in a["h"].items():
+        assert np.array_equal(h, L.mxfp4_activation(b["h"][s].astype(np.float32)).astype(np.float64))
