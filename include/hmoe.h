@@ -61,6 +61,8 @@ typedef enum hmoe_status {
 } hmoe_status;
 
 enum { HMOE_KEPT_NVFP4 = 0, HMOE_KEPT_MXFP4 = 1 };
+/* Activations of the kept tier's matmuls: 16-bit (W4A16) or MXFP4 (W4A4). */
+enum { HMOE_ACT_16BIT = 0, HMOE_ACT_MXFP4 = 1 };
 /* How hybrid_moe_forward runs the decode path (M <= 8). */
 enum { HMOE_DECODE_STAGED = 0, HMOE_DECODE_SINGLE_LAUNCH = 1 };
 enum { HMOE_TIER_KEPT = 0, HMOE_TIER_NF3 = 1 };
@@ -90,7 +92,14 @@ enum { HMOE_STAGE_ROUTE = 0, HMOE_STAGE_W13 = 1, HMOE_STAGE_W2 = 2, HMOE_STAGE_C
  *                W2, combine), the faster form on MI355X at every measured shape;
  *                HMOE_DECODE_SINGLE_LAUNCH (1): the whole decode forward in one
  *                persistent kernel ([P1] "How it works": the M <= 8 direct top-k path);
- *                both give the same bits. */
+ *                both give the same bits.
+ *   act_format   HMOE_ACT_16BIT (0): every expert W4A16 (x and h stay 16-bit, [P3]);
+ *                HMOE_ACT_MXFP4 (1): the kept tier, which must be MXFP4 (a bit map and
+ *                kept_format MXFP4), runs W4A4 ([P3] "What's in this PR": the W4A4
+ *                backends beside the W4A16 path): x before W13 and h (in fp32) before W2
+ *                are rounded to MXFP4 along K, blocks of 32, by the OCP MX v1.0
+ *                conversion, on MX-scaled matrix cores; the NF3 tail stays W4A16. Every
+ *                M then takes the grouped-GEMM path; decode_launch must be 0. */
 typedef struct hmoe_layer_desc {
     int32_t num_experts;
     int32_t hidden;
@@ -101,6 +110,7 @@ typedef struct hmoe_layer_desc {
     const uint8_t* bit_map;
     int32_t block_m;
     int32_t decode_launch;
+    int32_t act_format;
 } hmoe_layer_desc;
 
 /* Opaque, immutable after creation: concurrent calls on different streams with
@@ -117,6 +127,7 @@ typedef struct hmoe_layer_info {
     int32_t cap_kept, cap_nf3; /* align capacity per tier at max_tokens */
     int32_t fused_decode;      /* 1: hybrid_moe_forward runs M <= 8 as one launch */
     int32_t single_launch_available; /* 1: a single-launch decode exists for H and I */
+    int32_t act_format;        /* HMOE_ACT_16BIT or HMOE_ACT_MXFP4 */
 } hmoe_layer_info;
 
 /* Packed weights of both tiers, in the layouts above. Device pointers, owned by the
@@ -347,6 +358,17 @@ typedef struct hmoe_expert_src {
  * NULL, dst arrays of a non-empty tier NULL), HMOE_ERR_HIP. */
 hmoe_status moe_repack(const hmoe_layer* layer, const hmoe_expert_src* experts,
                        const hmoe_weights* dst, hipStream_t stream);
+
+/* The W4A4 activation quantiser on its own (test hook): rows x K fp32 values (device,
+ * K a multiple of 32, row-major) to MXFP4 by the OCP MX v1.0 conversion the layer uses
+ * for W4A4 activations ([P3]): per 32-block the shared exponent floor(log2 amax) - 2
+ * clamped to [-127, 127] (E8M0 byte 127 for an all-zero block), elements scaled by 2^-e
+ * and rounded to E2M1 nearest-even, saturating at 6, zero as code 0. codes: u8 [rows,
+ * K/2] (element 2j in the low nibble of byte j); scales: u8 [rows, K/32]. Pointers 16-byte
+ * aligned. Errors: HMOE_ERR_INVALID_ARG (rows < 0, K not a positive multiple of 32),
+ * HMOE_ERR_ALIGN, HMOE_ERR_HIP. */
+hmoe_status moe_quantize_mxfp4(const float* in, int32_t rows, int32_t K, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream);
 
 /* Static string naming a status code. */
 const char* moe_status_string(hmoe_status status);

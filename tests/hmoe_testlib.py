@@ -19,10 +19,12 @@ def fmt_code(packed: dict) -> int:
     return hm.KEPT_NVFP4 if OL.kept_format_of(packed) == "nvfp4" else hm.KEPT_MXFP4
 
 
-def make_layer(packed: dict, max_tokens: int, block_m: int = 0, decode_launch: int = 0):
+def make_layer(packed: dict, max_tokens: int, block_m: int = 0, decode_launch: int = 0,
+               act_format: int = 0):
     import weight_only_quantized_moe_amd as hm
     return hm.moe_layer_create(packed["E"], packed["H"], packed["I"], packed["top_k"], max_tokens,
-                               fmt_code(packed), packed["bit_map"], block_m, decode_launch)
+                               fmt_code(packed), packed["bit_map"], block_m, decode_launch,
+                               act_format)
 
 
 def scratch_for(layer):

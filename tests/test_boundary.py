@@ -55,6 +55,11 @@ def _create_status(**kw):
     ({"kept_format": 7}, INVALID),
     ({"block_m": 48}, INVALID),
     ({"decode_launch": 2}, INVALID),
+    ({"act_format": 2}, INVALID),
+    ({"act_format": 1}, INVALID),                                   # no bit map
+    ({"act_format": 1, "bit_map": [4] * 4 + [3] * 4}, INVALID),     # NVFP4 kept tier
+    ({"act_format": 1, "bit_map": [4] * 4 + [3] * 4, "kept_format": 1, "decode_launch": 1}, INVALID),
+    ({"act_format": 1, "bit_map": [4] * 4 + [3] * 4, "kept_format": 1}, OK),
     ({"hidden": 128, "inter": 128, "decode_launch": 1}, UNSUPPORTED),
     ({"bit_map": [4, 3, 5, 3, 3, 3, 3, 3]}, INVALID),
     ({"num_experts": 2048, "top_k": 2}, UNSUPPORTED),

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhmoe.so"
 
 KEPT_NVFP4, KEPT_MXFP4 = 0, 1
 DECODE_STAGED, DECODE_SINGLE_LAUNCH = 0, 1
+ACT_16BIT, ACT_MXFP4 = 0, 1
 TIER_KEPT, TIER_NF3 = 0, 1
 TENSOR_W13, TENSOR_W2 = 0, 1
 STAGE_ROUTE, STAGE_W13, STAGE_W2, STAGE_COMBINE = 0, 1, 2, 3
@@ -30,7 +31,7 @@ EXPORTED = (
     "moe_scratch_init",
     "moe_route", "moe_align", "moe_align_view", "moe_decode_view", "moe_topk_view",
     "hybrid_moe_forward", "hybrid_moe_forward_static", "hybrid_moe_forward_stage", "moe_dequant",
-    "moe_repack",
+    "moe_repack", "moe_quantize_mxfp4",
     "moe_status_string", "moe_last_error",
 )
 
@@ -44,14 +45,15 @@ class HmoeError(RuntimeError):
 class LayerDesc(Structure):
     _fields_ = [("num_experts", c_int32), ("hidden", c_int32), ("inter", c_int32),
                 ("top_k", c_int32), ("max_tokens", c_int32), ("kept_format", c_int32),
-                ("bit_map", c_void_p), ("block_m", c_int32), ("decode_launch", c_int32)]
+                ("bit_map", c_void_p), ("block_m", c_int32), ("decode_launch", c_int32),
+                ("act_format", c_int32)]
 
 
 class LayerInfo(Structure):
     _fields_ = [(n, c_int32) for n in (
         "num_experts", "hidden", "inter", "top_k", "max_tokens", "kept_format",
         "num_kept", "num_nf3", "block_m", "max_distinct", "cap_kept", "cap_nf3",
-        "fused_decode", "single_launch_available")]
+        "fused_decode", "single_launch_available", "act_format")]
 
 
 class Weights(Structure):
@@ -123,6 +125,8 @@ def load_library() -> ctypes.CDLL:
     lib.moe_dequant.restype = st
     lib.moe_repack.argtypes = [c_void_p, POINTER(ExpertSrc), POINTER(Weights), c_void_p]
     lib.moe_repack.restype = st
+    lib.moe_quantize_mxfp4.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+    lib.moe_quantize_mxfp4.restype = st
     lib.moe_status_string.argtypes = [c_int32]
     lib.moe_status_string.restype = c_char_p
     lib.moe_last_error.argtypes = []
@@ -172,13 +176,14 @@ class Layer:
 
 def moe_layer_create(num_experts: int, hidden: int, inter: int, top_k: int, max_tokens: int,
                      kept_format: int = KEPT_NVFP4, bit_map=None, block_m: int = 0,
-                     decode_launch: int = DECODE_STAGED) -> Layer:
+                     decode_launch: int = DECODE_STAGED, act_format: int = ACT_16BIT) -> Layer:
     lib = load_library()
     bm = None
     if bit_map is not None:
         bm = (ctypes.c_uint8 * num_experts)(*[int(v) for v in bit_map])
     d = LayerDesc(num_experts, hidden, inter, top_k, max_tokens, kept_format,
-                  ctypes.cast(bm, c_void_p) if bm is not None else None, block_m, decode_launch)
+                  ctypes.cast(bm, c_void_p) if bm is not None else None, block_m, decode_launch,
+                  act_format)
     h = c_void_p()
     _check(lib.moe_layer_create(byref(d), byref(h)))
     return Layer(h, bm)
@@ -317,6 +322,13 @@ def moe_repack(layer: Layer, experts, dst: "DeviceWeights", stream=None) -> None
             _ptr(ex.get("w13_g")), _ptr(ex["w2_lo"] if nf3 else ex["w2_q"]), _ptr(ex.get("w2_hi")),
             _ptr(ex["w2_s"]), _ptr(ex.get("w2_g")))
     _check(load_library().moe_repack(layer.handle, arr, byref(dst.struct), _stream(stream)))
+
+
+def moe_quantize_mxfp4(x, codes, scales, stream=None) -> None:
+    """x fp32 [rows, K] -> MXFP4 codes u8 [rows, K/2] and E8M0 scales u8 [rows, K/32]."""
+    rows, K = x.shape
+    _check(load_library().moe_quantize_mxfp4(_ptr(x), rows, K, _ptr(codes), _ptr(scales),
+                                             _stream(stream)))
 
 
 class DeviceWeights:

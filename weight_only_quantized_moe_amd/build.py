@@ -20,10 +20,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["host.cpp", "route.hip", "align.hip", "decode.hip", "prefill.hip", "dequant.hip",
-           "repack.hip", "noalloc.hip"]
+           "repack.hip", "noalloc.hip", "w4a4.hip"]
 # the streaming kernels must keep every value in registers: private-memory (scratch)
 # traffic shares the vector memory counter with the prefetched loads and drains them
-NO_SCRATCH = {"decode.hip", "prefill.hip"}
+NO_SCRATCH = {"decode.hip", "prefill.hip", "w4a4.hip"}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

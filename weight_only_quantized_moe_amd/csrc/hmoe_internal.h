@@ -29,6 +29,7 @@ struct ScratchPlan {
   size_t a_counts = 0;                     // int32 [E] slot counts per expert
   size_t a_slots[2] = {0, 0}, a_bexp[2] = {0, 0}, a_eoff[2] = {0, 0}, a_npad[2] = {0, 0};
   size_t h_pre = 0, o_pre = 0, x16_pre = 0, xe_pre = 0;
+  size_t mx_xq = 0, mx_xs = 0, mx_h32 = 0, mx_hq = 0, mx_hs = 0;   // W4A4 kept tier
   size_t total = 0;
 };
 
@@ -41,6 +42,7 @@ struct GemvTiling {
 struct Layer {
   int E = 0, H = 0, I = 0, k = 0, max_tokens = 0;
   int kept_format = HMOE_KEPT_NVFP4;  // effective
+  int act_format = HMOE_ACT_16BIT;    // HMOE_ACT_MXFP4: the kept tier runs W4A4
   int block_m = 32;
   bool has_map = false;
   std::vector<uint8_t> bit_map;
@@ -83,9 +85,19 @@ hipError_t launch_decode_fused(const Layer& L, const hmoe_weights& W, const uint
                                hipStream_t s);
 hipError_t launch_sync_clear(const Layer& L, void* scratch, hipStream_t s);
 
-// prefill.hip: one stage (HMOE_STAGE_W13 / _W2 / _COMBINE) of the prefill path
+// prefill.hip: one stage (HMOE_STAGE_W13 / _W2 / _COMBINE) of the prefill path;
+// nf3_only: the GEMMs skip the kept tier's blocks (the W4A4 kept tier has its own)
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
-                          uint16_t* y, void* scratch, int stage, hipStream_t s);
+                          uint16_t* y, void* scratch, int stage, hipStream_t s,
+                          bool nf3_only = false);
+
+// w4a4.hip: the W4A4 kept tier's part of a stage (ROUTE: x to MXFP4; W13: GEMM + h to
+// MXFP4; W2: GEMM), and the MXFP4 activation quantiser (rows x K, bf16 or fp32 input;
+// rows at or past *nrows skipped when nrows is given)
+hipError_t launch_w4a4(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
+                       void* scratch, int stage, hipStream_t s);
+hipError_t launch_mx_quant(const void* in, bool bf16, int rows, int K, const int32_t* nrows,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // prefill.hip: tokens to fp16 with a per-token power-of-two scale (prefill input)
 hipError_t launch_prefill_x16(const Layer& L, const uint16_t* x, int M, void* scratch,

@@ -69,7 +69,7 @@ void plan_scratch(hmoe::Layer& L) {
     P.a_eoff[t] = take((size_t)(ne + 1) * 4);
     P.a_npad[t] = take(4);
   }
-  if (L.max_tokens > hmoe::kDecodeMaxM) {
+  if (L.max_tokens > hmoe::kDecodeMaxM || L.act_format == HMOE_ACT_MXFP4) {
     P.h_pre = take((size_t)(L.cap[0] + L.cap[1]) * L.I * 2);
     P.o_pre = take(mk * L.H * 4);
     P.x16_pre = take((size_t)L.max_tokens * L.H * 2);
@@ -79,6 +79,13 @@ void plan_scratch(hmoe::Layer& L) {
     P.o_pre = take(0);
     P.x16_pre = take(0);
     P.xe_pre = take(0);
+  }
+  if (L.act_format == HMOE_ACT_MXFP4) {
+    P.mx_xq = take((size_t)L.max_tokens * L.H / 2);
+    P.mx_xs = take((size_t)L.max_tokens * L.H / 32);
+    P.mx_h32 = take((size_t)L.cap[0] * L.I * 4);
+    P.mx_hq = take((size_t)L.cap[0] * L.I / 2);
+    P.mx_hs = take((size_t)L.cap[0] * L.I / 32);
   }
   P.total = off;
 }
@@ -150,6 +157,12 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
     return fail(HMOE_ERR_INVALID_ARG, "block_m must be 0, 16, 32, 64 or 128");
   if (d->decode_launch != HMOE_DECODE_STAGED && d->decode_launch != HMOE_DECODE_SINGLE_LAUNCH)
     return fail(HMOE_ERR_INVALID_ARG, "unknown decode_launch");
+  if (d->act_format != HMOE_ACT_16BIT && d->act_format != HMOE_ACT_MXFP4)
+    return fail(HMOE_ERR_INVALID_ARG, "unknown act_format");
+  if (d->act_format == HMOE_ACT_MXFP4 && (!d->bit_map || d->kept_format != HMOE_KEPT_MXFP4))
+    return fail(HMOE_ERR_INVALID_ARG, "W4A4 needs a bit map and an MXFP4 kept tier");
+  if (d->act_format == HMOE_ACT_MXFP4 && d->decode_launch != HMOE_DECODE_STAGED)
+    return fail(HMOE_ERR_INVALID_ARG, "the single-launch decode runs W4A16 only");
   if (d->num_experts > hmoe::kMaxExperts) return fail(HMOE_ERR_UNSUPPORTED, "num_experts > 1024");
   if (d->top_k > hmoe::kMaxTopK) return fail(HMOE_ERR_UNSUPPORTED, "top_k > 16");
   if (d->hidden % 128 || d->inter % 128)
@@ -173,6 +186,7 @@ hmoe_status moe_layer_create(const hmoe_layer_desc* d, hmoe_layer** out) {
   L.has_map = d->bit_map != nullptr;
   L.kept_format = L.has_map ? d->kept_format : HMOE_KEPT_NVFP4;
   L.block_m = d->block_m ? d->block_m : auto_block_m(d->max_tokens, d->top_k, d->num_experts);
+  L.act_format = d->act_format;
   L.bit_map.assign(L.E, 4);
   if (L.has_map) memcpy(L.bit_map.data(), d->bit_map, L.E);
   for (int e = 0; e < L.E; ++e) {
@@ -238,6 +252,7 @@ hmoe_status moe_layer_query(const hmoe_layer* layer, hmoe_layer_info* out) {
   out->cap_nf3 = L.cap[1];
   out->fused_decode = L.fused_decode ? 1 : 0;
   out->single_launch_available = L.single_available ? 1 : 0;
+  out->act_format = L.act_format;
   return HMOE_OK;
 }
 
@@ -333,7 +348,8 @@ hmoe_status hybrid_moe_forward_stage(const hmoe_layer* layer, const hmoe_weights
   if (hmoe_status st = check_scratch(L, scratch, scratch_bytes)) return st;
   if (!x || !router_logits || !y || !aligned(x, 16) || !aligned(router_logits, 16) || !aligned(y, 16))
     return fail(HMOE_ERR_ALIGN, "x, router_logits and y must be non-NULL and 16-byte aligned");
-  const bool decode = M <= hmoe::kDecodeMaxM;
+  const bool w4a4 = L.act_format == HMOE_ACT_MXFP4;
+  const bool decode = M <= hmoe::kDecodeMaxM && !w4a4;
   hipError_t err;
   if (stage == HMOE_STAGE_ROUTE) {
     if (decode) {
@@ -345,11 +361,14 @@ hmoe_status hybrid_moe_forward_stage(const hmoe_layer* layer, const hmoe_weights
                                reinterpret_cast<float*>(b + L.plan.topk_w), stream);
       if (err == hipSuccess) err = hmoe::launch_align(L, ids, M, scratch, stream);
       if (err == hipSuccess) err = hmoe::launch_prefill_x16(L, x, M, scratch, stream);
+      if (err == hipSuccess && w4a4) err = hmoe::launch_w4a4(L, *weights, x, M, scratch, stage, stream);
     }
   } else if (decode) {
     err = hmoe::launch_decode(L, *weights, x, M, y, scratch, stage, stream);
   } else {
-    err = hmoe::launch_prefill(L, *weights, x, M, y, scratch, stage, stream);
+    err = hmoe::launch_prefill(L, *weights, x, M, y, scratch, stage, stream, w4a4);
+    if (err == hipSuccess && w4a4 && stage != HMOE_STAGE_COMBINE)
+      err = hmoe::launch_w4a4(L, *weights, x, M, scratch, stage, stream);
   }
   if (err != hipSuccess) return hip_fail(err, "kernel launch");
   return HMOE_OK;
@@ -489,6 +508,17 @@ hmoe_status moe_repack(const hmoe_layer* layer, const hmoe_expert_src* experts,
     hipError_t err = hmoe::launch_repack(batch, stream);
     if (err != hipSuccess) return hip_fail(err, "repack");
   }
+  return HMOE_OK;
+}
+
+hmoe_status moe_quantize_mxfp4(const float* in, int32_t rows, int32_t K, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+  if (rows < 0 || K <= 0 || K % 32) return fail(HMOE_ERR_INVALID_ARG, "rows >= 0 and K a positive multiple of 32");
+  if (rows == 0) return HMOE_OK;
+  if (!in || !codes || !scales || !aligned(in, 16) || !aligned(codes, 16))
+    return fail(HMOE_ERR_ALIGN, "in, codes and scales must be non-NULL, in and codes 16-byte aligned");
+  hipError_t err = hmoe::launch_mx_quant(in, false, rows, K, nullptr, codes, scales, stream);
+  if (err != hipSuccess) return hip_fail(err, "quantise launch");
   return HMOE_OK;
 }
 

@@ -704,7 +704,7 @@ hipError_t launch_prefill_x16(const Layer& L, const uint16_t* x, int M, void* sc
 }
 
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
-                          uint16_t* y, void* scratch, int stage, hipStream_t s) {
+                          uint16_t* y, void* scratch, int stage, hipStream_t s, bool nf3_only) {
   char* base = static_cast<char*>(scratch);
   const ScratchPlan& P = L.plan;
   float* w = reinterpret_cast<float*>(base + P.topk_w);
@@ -724,7 +724,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
   const int ns = M * L.k;
   const int cap0 = ns + (L.E4 < ns ? L.E4 : ns) * (bm - 1);
   const int cap1 = ns + (L.E3 < ns ? L.E3 : ns) * (bm - 1);
-  a.nblk0 = L.E4 > 0 ? (cap0 + bm - 1) / bm : 0;
+  a.nblk0 = (L.E4 > 0 && !nf3_only) ? (cap0 + bm - 1) / bm : 0;
   a.nblk1 = L.E3 > 0 ? (cap1 + bm - 1) / bm : 0;
   a.hrow1 = L.cap[0];
   a.I = L.I;
