@@ -10,8 +10,11 @@ Default run: both halves of the metric.
     M = 1, 2, 4 points of the decode sweep beside it;
   * prefill: the GLM-class layer (E=256, H=6144, I=2048, top-8, 64 NVFP4 + 192 NF3,
     skewed routing) at M = 4096, reported under "prefill" with its TFLOP/s.
+  * W4A4: the GLM-class MXFP4 + NF3 layer at M = 512 with the kept tier's activations in
+    MXFP4 on MX-scaled matrix cores, reported under "w4a4" beside the same layer as W4A16.
 --workload NAME runs one workload alone: qwen_decode, glm_decode (M=8), glm_prefill
-(M=4096), glm_mxfp4 (MXFP4 kept tier, M=512) or glm_uniform (no bit map, M=512).
+(M=4096), glm_mxfp4 (MXFP4 kept tier, M=512; --w4a4 for W4A4) or glm_uniform (no bit
+map, M=512).
 
 One step is one hybrid_moe_forward over one batch: routing, grouping or align,
 both tiers' W13 + SwiGLU, W2 + weighted combine. Steps replay HIP graphs of the
@@ -107,7 +110,7 @@ def pmc_traffic(kernel_key, src_hash, launches_bytes):
 
 
 def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=None,
-            decode_launch=0):
+            decode_launch=0, act_format=0):
     """Times `steps` graph replays of the forward at w.M; returns a result dict."""
     import numpy as np
     import torch
@@ -121,7 +124,8 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
         log(f"{w.name}: generated packed layer in {time.time() - t0:.1f}s")
     bm = packed["bit_map"]
     fmt = hm.KEPT_NVFP4 if packed["kept_format"] == "nvfp4" else hm.KEPT_MXFP4
-    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, block_m or 0, decode_launch)
+    layer = hm.moe_layer_create(w.E, w.H, w.I, w.top_k, w.M, fmt, bm, block_m or 0, decode_launch,
+                                act_format)
     block_m = hm.moe_layer_query(layer)["block_m"]
     base = hm.DeviceWeights(packed)
     layer_bytes = base.nbytes()
@@ -209,7 +213,8 @@ def measure(w, steps, warmup, copies=None, stage_steps=30, packed=None, block_m=
            "layer_bytes_resident": layer_bytes, "desc": describe(w, packed)}
     io_bytes = M * w.H * 2 + M * w.E * 4 + M * w.H * 2        # x, logits, y
     flops = 6.0 * M * k * w.H * w.I
-    if M <= hm.DECODE_MAX_M:
+    res["act_format"] = act_format
+    if M <= hm.DECODE_MAX_M and not act_format:
         v = hm.moe_decode_view(layer, scratch)
         counts = v["counts"].cpu().numpy()
         nd, nk = int(counts[0]), int(counts[1])
@@ -261,7 +266,9 @@ def roofline(w, r, src, decode):
     intensity = r["flops"] / r["layer_bytes"]
     hbm = decode or intensity < RIDGE_FLOP_PER_BYTE
     fused = decode and r.get("fused_launch_us") is not None
-    key = ("decode_fused_" if fused else "decode_w13_" if decode else "prefill_w13_") + w.name
+    w4a4 = bool(r.get("act_format"))
+    key = ("decode_fused_" if fused else "decode_w13_" if decode else
+           "w4a4_w13_" if w4a4 else "prefill_w13_") + w.name
     if fused:
         work, scale, peak, unit = r["layer_bytes"], 1e9, HBM_PEAK_GBPS, "GB/s"
     elif hbm:
@@ -270,6 +277,8 @@ def roofline(w, r, src, decode):
         work, scale, peak, unit = r["w13_flops"], 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     kernel = ("decode_fused_kernel (the whole decode forward)" if fused
               else "w13_gemv_kernel (decode W13 + SwiGLU)" if decode
+              else "W13 stage: mx_gemm_kernel<W13> (kept tier, W4A4) + grouped_gemm_kernel<W13> "
+                   "(NF3 tier) + h quantiser" if w4a4
               else "grouped_gemm_kernel<W13> (prefill W13 + SwiGLU)")
     ev_us = r["fused_launch_us"] if fused else r["w13_launch_us"]
     prof_us, prof = rocprof_launch_us(key, src)
@@ -336,6 +345,8 @@ def workload_record(w, r, decode, args, steps):
            "roofline": roofline(w, r, src, decode)}
     if not decode:
         rec["block_m"] = r["block_m"]
+    if r.get("act_format"):
+        rec["activations"] = "kept tier MXFP4 (W4A4), NF3 tail bf16/fp16 (W4A16)"
     return rec
 
 
@@ -412,6 +423,8 @@ def main():
                     help="run this workload alone (default: Qwen-shaped decode M=8 with its sweep, "
                          "and GLM-class prefill M=4096)")
     ap.add_argument("--m", type=int, default=None, help="override the batch size")
+    ap.add_argument("--w4a4", action="store_true",
+                    help="with --workload glm_mxfp4: the kept tier as W4A4 (MXFP4 activations)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies to rotate")
     ap.add_argument("--no-sweep", action="store_true", help="skip the M=1,2,4 decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -457,7 +470,8 @@ def main():
     w = workload(args.workload or "qwen_decode", args.m)
     decode = w.M <= hm.DECODE_MAX_M
     log(f"measuring {w.name} (M={w.M}), {args.steps} steps after {args.warmup} warm-up")
-    r = measure(w, args.steps, args.warmup, args.copies, block_m=args.block_m)
+    r = measure(w, args.steps, args.warmup, args.copies, block_m=args.block_m,
+                act_format=1 if args.w4a4 else 0)
     rec = workload_record(w, r, decode, args, args.steps)
     ms = r["ms_per_step"]
     out = {
@@ -536,6 +550,19 @@ def main():
             cb["value_tflops"] = rp["flops"] * cb["value"] / wp.M / 1e12
             prec["cpu_baseline"] = cb
         out["prefill"] = prec
+        del rp
+        # the W4A4 kept tier (MXFP4 weights and activations on MX-scaled matrix cores) on
+        # the GLM-class MXFP4 + NF3 layer at M = 512, beside the same layer as W4A16
+        wx = workload("glm_mxfp4", None)
+        log(f"measuring {wx.name} (M={wx.M}) W4A4 and W4A16")
+        rx = measure(wx, psteps, min(args.warmup, 10), args.copies, act_format=1)
+        xrec = workload_record(wx, rx, False, args, psteps)
+        r16 = measure(wx, psteps, min(args.warmup, 10), args.copies, packed=rx["packed"])
+        xrec["w4a16_same_layer"] = {"ms_per_step": r16["ms_per_step"],
+                                    "tok_per_s": wx.M / (r16["ms_per_step"] * 1e-3),
+                                    "stage_us": dict(zip(["route", "w13", "w2", "combine"],
+                                                         [round(v, 2) for v in r16["stage_us"]]))}
+        out["w4a4"] = xrec
     print(json.dumps(out), flush=True)
 
 

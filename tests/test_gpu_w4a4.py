@@ -55,9 +55,12 @@ def test_w4a4_tiny_layer(hm, M, block_m):
     y, s = run_forward(layer, wts, x, lg)
     ref = OL.forward(packed, x, lg, act_format="mxfp4")["y"]
     check_output(y, ref, f"W4A4 tiny M={M} bm={block_m}")
-    # the bar separates the formats: the W4A16 result is far outside it
-    w16 = OL.forward(packed, x, lg)["y"]
-    assert np.abs(w16 - ref).max() > 0.1 * np.sqrt(np.mean(ref ** 2))
+    # the bar separates the formats: where the kept tier is used, the W4A16 result is
+    # far outside it (the NF3 tail is W4A16 in both)
+    tier, _ = OL.tier_map(packed["bit_map"], packed["E"])
+    if np.any(tier[OL.route(lg, packed["top_k"])[0]] == OL.KEPT):
+        w16 = OL.forward(packed, x, lg)["y"]
+        assert np.abs(w16 - ref).max() > 0.1 * np.sqrt(np.mean(ref ** 2))
     y2, _ = run_forward(layer, wts, x, lg, s)
     assert np.array_equal(y, y2), "W4A4 forward not bitwise reproducible"
 
