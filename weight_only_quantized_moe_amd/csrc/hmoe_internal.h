@@ -86,14 +86,15 @@ hipError_t launch_decode_fused(const Layer& L, const hmoe_weights& W, const uint
 hipError_t launch_sync_clear(const Layer& L, void* scratch, hipStream_t s);
 
 // prefill.hip: one stage (HMOE_STAGE_W13 / _W2 / _COMBINE) of the prefill path;
-// nf3_only: the GEMMs skip the kept tier's blocks (the W4A4 kept tier has its own)
+// nf3_only (W4A4 layers): the W4A16 GEMM covers the NF3 tier and the same launch runs
+// the kept tier on MX matrix cores
 hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
                           uint16_t* y, void* scratch, int stage, hipStream_t s,
                           bool nf3_only = false);
 
-// w4a4.hip: the W4A4 kept tier's part of a stage (ROUTE: x to MXFP4; W13: GEMM + h to
-// MXFP4; W2: GEMM), and the MXFP4 activation quantiser (rows x K, bf16 or fp32 input;
-// rows at or past *nrows skipped when nrows is given)
+// w4a4.hip: the W4A4 kept tier's quantisation around the GEMM launches (ROUTE: x to
+// MXFP4; W13: h to MXFP4), and the MXFP4 activation quantiser (rows x K, bf16 or fp32
+// input; rows at or past *nrows skipped when nrows is given)
 hipError_t launch_w4a4(const Layer& L, const hmoe_weights& W, const uint16_t* x, int M,
                        void* scratch, int stage, hipStream_t s);
 hipError_t launch_mx_quant(const void* in, bool bf16, int rows, int K, const int32_t* nrows,

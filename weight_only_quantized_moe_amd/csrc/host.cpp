@@ -366,8 +366,10 @@ hmoe_status hybrid_moe_forward_stage(const hmoe_layer* layer, const hmoe_weights
   } else if (decode) {
     err = hmoe::launch_decode(L, *weights, x, M, y, scratch, stage, stream);
   } else {
+    // W4A4: the GEMM launches run both tiers (kept tier on MX matrix cores); the W13
+    // stage then rounds the kept tier's h to MXFP4
     err = hmoe::launch_prefill(L, *weights, x, M, y, scratch, stage, stream, w4a4);
-    if (err == hipSuccess && w4a4 && stage != HMOE_STAGE_COMBINE)
+    if (err == hipSuccess && w4a4 && stage == HMOE_STAGE_W13)
       err = hmoe::launch_w4a4(L, *weights, x, M, scratch, stage, stream);
   }
   if (err != hipSuccess) return hip_fail(err, "kernel launch");

@@ -38,6 +38,7 @@
 
 #include "device_common.h"
 #include "hmoe_internal.h"
+#include "mx_gemm.h"
 
 namespace hmoe {
 
@@ -574,13 +575,12 @@ __device__ __forceinline__ void gemm_tile_any(const PrefillArgs& a, int tier, in
 // that class are neither multiplied nor written, by this launch or the W2 launch (the
 // same slots give it the same class).
 template <int BMAX, bool W13>
-__global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs a) {
+__device__ __forceinline__ void grouped_gemm_block(const PrefillArgs& a, int L) {
   // A 1-D grid. The dispatcher hands consecutive block ids to the eight XCDs in
   // turn (id L runs on XCD L % 8), so id L is given a group of kXcdGroup expert blocks
   // owned by XCD L % 8, and the ids of one XCD walk a group's column tiles with its
   // blocks innermost: an expert block's activation rows and the weight tile its
   // group's blocks share stay in that XCD's L2.
-  const int L = blockIdx.x;
   const int idx = L >> 3;
   const int per_group = a.ntile * kXcdGroup;
   const int grp = idx / per_group;
@@ -613,6 +613,26 @@ __global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs
     if (cls == 64) return gemm_tile_any<64, BMAX, W13>(a, tier, r0, loc, tile, smem);
   }
   gemm_tile_any<BMAX, BMAX, W13>(a, tier, r0, loc, tile, smem);
+}
+
+template <int BMAX, bool W13>
+__global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_kernel(PrefillArgs a) {
+  grouped_gemm_block<BMAX, W13>(a, blockIdx.x);
+}
+
+// The W4A4 layer's GEMM launch: the NF3 tier's W4A16 blocks (ids below nf3_grid, the
+// grouped_gemm_kernel grid) and then the kept tier's MX blocks (column tiles fastest), so
+// both tiers run in one launch and overlap on the GPU.
+template <int BMAX, bool W13>
+__global__ __launch_bounds__(kPfThreads, 2) void grouped_gemm_w4a4_kernel(PrefillArgs a, MxArgs m,
+                                                                          int nf3_grid, int mx_tiles) {
+  const int L = blockIdx.x;
+  if (L < nf3_grid) {
+    grouped_gemm_block<BMAX, W13>(a, L);
+  } else {
+    const int i = L - nf3_grid;
+    mx_gemm_tile<BMAX, W13>(m, i / mx_tiles, i - (i / mx_tiles) * mx_tiles);
+  }
 }
 
 // x16[t] = fp16(x[t] * 2^-e[t]), e[t] putting the token's largest |x| in [2^14, 2^15);
@@ -669,6 +689,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
 }
 
 typedef void (*GemmFn)(PrefillArgs);
+typedef void (*GemmW4a4Fn)(PrefillArgs, MxArgs, int, int);
 
 template <bool W13>
 static GemmFn pick_gemm(int bm) {
@@ -679,6 +700,38 @@ static GemmFn pick_gemm(int bm) {
     case 128: return grouped_gemm_kernel<128, W13>;
   }
   return nullptr;
+}
+
+template <bool W13>
+static GemmW4a4Fn pick_gemm_w4a4(int bm) {
+  switch (bm) {
+    case 16: return grouped_gemm_w4a4_kernel<16, W13>;
+    case 32: return grouped_gemm_w4a4_kernel<32, W13>;
+    case 64: return grouped_gemm_w4a4_kernel<64, W13>;
+    case 128: return grouped_gemm_w4a4_kernel<128, W13>;
+  }
+  return nullptr;
+}
+
+// one GEMM launch: the grouped GEMM alone, or (W4A4 layers) with the kept tier's MX
+// blocks after the NF3 tier's
+template <bool W13>
+static hipError_t launch_gemm(const Layer& L, const hmoe_weights& W, int M, void* scratch,
+                              const PrefillArgs& b, unsigned grid, bool w4a4, hipStream_t s) {
+  if (!w4a4) {
+    GemmFn fn = pick_gemm<W13>(L.block_m);
+    if (!fn) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kPfThreads), 0, s, b);
+    return hipGetLastError();
+  }
+  GemmW4a4Fn fn = pick_gemm_w4a4<W13>(L.block_m);
+  if (!fn) return hipErrorInvalidValue;
+  const MxArgs m = mx_args(L, W, M, scratch, W13 ? HMOE_STAGE_W13 : HMOE_STAGE_W2);
+  const int tiles = mx_tiles(L, W13);
+  const unsigned total = grid + (unsigned)(m.nblk * tiles);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3(total), dim3(kPfThreads), 0, s, b, m, (int)grid, tiles);
+  return hipGetLastError();
 }
 
 // scale rows of whole, aligned 16-byte vectors of 8 K steps (512 K values), both tiers
@@ -745,10 +798,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     b.h_out = h;
     b.ntile = L.I / (kBN / 2);
     b.vec_scales = vec_scales_ok(b);
-    GemmFn fn = pick_gemm<true>(bm);
-    if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(gemm_grid(nblk, b.ntile)), dim3(kPfThreads), 0, s, b);
-    return hipGetLastError();
+    return launch_gemm<true>(L, W, M, scratch, b, nblk > 0 ? gemm_grid(nblk, b.ntile) : 0u, nf3_only, s);
   }
   if (stage == HMOE_STAGE_W2) {
     PrefillArgs c = a;
@@ -762,10 +812,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     c.topk_w = w;
     c.ntile = L.H / kBN;
     c.vec_scales = vec_scales_ok(c);
-    GemmFn fn = pick_gemm<false>(bm);
-    if (!fn) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3(gemm_grid(nblk, c.ntile)), dim3(kPfThreads), 0, s, c);
-    return hipGetLastError();
+    return launch_gemm<false>(L, W, M, scratch, c, nblk > 0 ? gemm_grid(nblk, c.ntile) : 0u, nf3_only, s);
   }
   if (stage == HMOE_STAGE_COMBINE) {
     const size_t n = (size_t)M * (L.H / 4);
