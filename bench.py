@@ -85,6 +85,15 @@ def expert_bytes(packed):
     return out
 
 
+def kernel_sources(decode, w4a4):
+    """The source files of a workload's dominant kernel (what its profiles depend on)."""
+    if decode:
+        return ("decode.hip", "route_common.h", "device_common.h")
+    if w4a4:
+        return ("prefill.hip", "mx_gemm.h", "w4a4.hip", "device_common.h")
+    return ("prefill.hip", "mx_gemm.h", "device_common.h")
+
+
 def source_hash(*files):
     h = hashlib.sha256()
     for f in files:
@@ -332,7 +341,7 @@ def cpu_baseline(packed, x_bits, logits, runs, tokens=None):
 def workload_record(w, r, decode, args, steps):
     """The fields one workload contributes to the JSON line."""
     ms = r["ms_per_step"]
-    src = source_hash("decode.hip" if decode else "prefill.hip", "device_common.h")
+    src = source_hash(*kernel_sources(decode, bool(r.get("act_format"))))
     rec = {"workload": r["desc"], "M": w.M, "ms_per_step": ms, "tok_per_s": w.M / (ms * 1e-3),
            "steps": steps, "weight_copies_rotated": r["copies"],
            "hbm_gbps": r["layer_bytes"] / (ms * 1e-3) / 1e9,
