@@ -3,6 +3,8 @@
 // PR #42428, "What's in this PR": W4A4 backends beside the W4A16 path.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "hmoe_internal.h"
 
@@ -40,12 +42,13 @@ MxArgs mx_args(const Layer& L, const hmoe_weights& W, int M, void* scratch, int 
 
 // Block: BM slot rows of one kept-tier align block x kMxBN weight rows (W13: 64 gate
 // rows and the matching 64 up rows, so the block makes 64 h columns; W2: 128 output
-// columns). Four waves split it 2 x 2 (1 x 4 for BM = 16); each wave keeps MT x NT
-// 16x16 tiles in registers and loads, per 128-K step, one 16-byte fragment and one scale
-// byte per tile row and per tile column, the next step's already in flight.
+// columns). Four waves split it 2 x 2 (1 x 4 up to 32 rows, so that no two waves load
+// the same weight fragments); each wave keeps MT x NT 16x16 tiles in registers and
+// loads, per 128-K step, one 16-byte fragment per tile row and per tile column, the next
+// step's already in flight, and the E8M0 bytes of its rows (see below).
 template <int BM, bool W13>
 __device__ __forceinline__ void mx_gemm_tile(const MxArgs& a, int blk, int tile) {
-  constexpr int WAVES_M = BM >= 32 ? 2 : 1;
+  constexpr int WAVES_M = BM >= 64 ? 2 : 1;
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int MT = BM / WAVES_M / 16;
   constexpr int NT = kMxBN / WAVES_N / 16;
@@ -132,16 +135,84 @@ __device__ __forceinline__ void mx_gemm_tile(const MxArgs& a, int blk, int tile)
     }
   };
   const int steps = a.K / kMxBK;
-  Frag f0, f1;
-  load(0, f0);
-  int st = 0;
-  for (; st + 2 <= steps; st += 2) {
-    load(st + 1, f1);
-    mma(f0);
-    if (st + 2 < steps) load(st + 2, f0);
-    mma(f1);
+  // Tiles of up to 32 rows, whose waves issue one scale load per MFMA or more, with
+  // scale rows of whole, aligned 16-byte vectors (K a multiple of 512): a lane's E8M0
+  // bytes of four consecutive steps (byte g of dword i is block g of step 4 q + i) come
+  // in one 16-byte load per tile row and tile column, a quarter of the scale loads.
+  // Every load of that loop is unconditional (steps past the last re-read the last
+  // group), so the compiler's waits count exactly the loads each use needs.
+  const bool vs = BM <= 32 && SB % 16 == 0 && (reinterpret_cast<uintptr_t>(a.as) % 16) == 0 &&
+                  (reinterpret_cast<uintptr_t>(a.ws) % 16) == 0;
+  if (BM <= 32 && vs) {
+    struct Codes {
+      uint4 aq[MT], bq[NT];
+    };
+    struct SVec {
+      uint4 a[MT], b[NT];
+    };
+    auto load_codes = [&](int st, Codes& c) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) c.aq[mt] = *reinterpret_cast<const uint4*>(aqp[mt] + st * (kMxBK / 2));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) c.bq[nt] = *reinterpret_cast<const uint4*>(bq[nt] + st * (kMxBK / 2));
+    };
+    // the rows' scale vectors of steps 4 q .. 4 q + 3 (asp / bs point at byte g)
+    auto load_sv = [&](int q, SVec& v) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) v.a[mt] = *reinterpret_cast<const uint4*>(asp[mt] - g + 16 * q);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) v.b[nt] = *reinterpret_cast<const uint4*>(bs[nt] - g + 16 * q);
+    };
+    auto word = [](const uint4& v, auto I) -> uint32_t {
+      if constexpr (decltype(I)::value == 0) return v.x;
+      else if constexpr (decltype(I)::value == 1) return v.y;
+      else if constexpr (decltype(I)::value == 2) return v.z;
+      else return v.w;
+    };
+    auto mma_v = [&](const Codes& c, const SVec& v, auto I) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x8 av = {(int)c.aq[mt].x, (int)c.aq[mt].y, (int)c.aq[mt].z, (int)c.aq[mt].w, 0, 0, 0, 0};
+        const int sa = (int)__builtin_amdgcn_ubfe(word(v.a[mt], I), 8 * g, 8);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const i32x8 bv = {(int)c.bq[nt].x, (int)c.bq[nt].y, (int)c.bq[nt].z, (int)c.bq[nt].w, 0, 0, 0, 0};
+          const int sb = (int)__builtin_amdgcn_ubfe(word(v.b[nt], I), 8 * g, 8);
+          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[mt][nt], 4, 4, 0,
+                                                                          sa, 0, sb);
+        }
+      }
+    };
+    const int last = steps - 1, nq = steps / 4;
+    Codes c0, c1;
+    SVec v0, v1;
+    load_sv(0, v0);
+    load_codes(0, c0);
+    for (int q = 0; q < nq; ++q) {
+      const int st = 4 * q;
+      load_sv(min(q + 1, nq - 1), v1);
+      load_codes(st + 1, c1);
+      mma_v(c0, v0, std::integral_constant<int, 0>{});
+      load_codes(st + 2, c0);
+      mma_v(c1, v0, std::integral_constant<int, 1>{});
+      load_codes(st + 3, c1);
+      mma_v(c0, v0, std::integral_constant<int, 2>{});
+      load_codes(min(st + 4, last), c0);
+      mma_v(c1, v0, std::integral_constant<int, 3>{});
+      v0 = v1;
+    }
+  } else {
+    Frag f0, f1;
+    load(0, f0);
+    int st = 0;
+    for (; st + 2 <= steps; st += 2) {
+      load(st + 1, f1);
+      mma(f0);
+      if (st + 2 < steps) load(st + 2, f0);
+      mma(f1);
+    }
+    if (st < steps) mma(f0);
   }
-  if (st < steps) mma(f0);
 
   // epilogue: lane holds rows 4 g + q of each 16-row tile, column j
 #pragma unroll
