@@ -225,10 +225,12 @@ hmoe_status moe_layer_query(const hmoe_layer* layer, hmoe_layer_info* out);
  * allocates the buffer and passes it to every call. */
 hmoe_status moe_scratch_bytes(const hmoe_layer* layer, size_t* bytes);
 
-/* Prepares a scratch buffer for its first forward: zero-fills the counters the
+/* Prepares a scratch buffer for this layer's forwards: zero-fills the counters the
  * single-launch decode synchronises its workgroups with (every forward leaves them
- * zero again). A scratch buffer that was allocated zero-filled needs no call. Enqueued on
- * `stream` (a fill kernel, no memset, so it may be captured).
+ * zero again). A scratch buffer that was allocated zero-filled and serves only this layer
+ * needs no call; one that other layers or other work also write needs a call before each
+ * of this layer's M <= 8 forwards that follows such a write. Enqueued on `stream` (a fill
+ * kernel, no memset, so it may be captured).
  * Errors: HMOE_ERR_INVALID_ARG, HMOE_ERR_ALIGN, HMOE_ERR_SCRATCH, HMOE_ERR_HIP. */
 hmoe_status moe_scratch_init(const hmoe_layer* layer, void* scratch, size_t scratch_bytes,
                              hipStream_t stream);
@@ -271,7 +273,11 @@ hmoe_status moe_topk_view(const hmoe_layer* layer, void* scratch, int32_t** topk
  * whichever workgroup finishes a 64-row output group last); both give the same bits. M > 8 takes the prefill path (route, per-tier align, grouped GEMM W13 +
  * SwiGLU, grouped GEMM W2 + weighted combine). M = 0 is a no-op returning HMOE_OK.
  * Never allocates, synchronises or reads back: capturable in a HIP graph at fixed M.
- * The scratch must have been zero-filled or passed through moe_scratch_init once.
+ * The single-launch decode needs its counters in the scratch at zero when it starts:
+ * every forward leaves them zero, so a buffer that was zero-filled or passed through
+ * moe_scratch_init once needs nothing more, as long as nothing else writes it; after the
+ * buffer served another layer (whose regions differ) or any other use, call
+ * moe_scratch_init again before this layer's next M <= 8 forward.
  * Errors: HMOE_ERR_INVALID_ARG (null layer/weights, M < 0, a needed weight array NULL),
  * HMOE_ERR_CAPACITY, HMOE_ERR_SCRATCH, HMOE_ERR_ALIGN, HMOE_ERR_HIP. */
 hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weights,
@@ -286,6 +292,9 @@ hmoe_status hybrid_moe_forward(const hmoe_layer* layer, const hmoe_weights* weig
  * hipGetSymbolAddress on the first call on each device; the current device must be the
  * stream's). Allocates nothing. All calls on one GPU share that GPU's array, so calls
  * that overlap in time on one GPU (other streams, other threads) race; serialise them.
+ * The array keeps the last call's contents: before a single-launch decode forward the
+ * call clears that layer's counters (a fill kernel on the stream), so layers of any
+ * kind can take turns on it.
  * Arguments and results as hybrid_moe_forward.
  * Errors: HMOE_ERR_SCRATCH when moe_scratch_bytes(layer) exceeds 64 MiB (checked before
  * any device call), HMOE_ERR_HIP when the array's address cannot be obtained, and the

@@ -412,6 +412,13 @@ hmoe_status hybrid_moe_forward_static(const hmoe_layer* layer, const hmoe_weight
   void* scratch = nullptr;
   hipError_t err = hmoe::static_scratch(&scratch);
   if (err != hipSuccess) return hip_fail(err, "static scratch address");
+  // every layer on this GPU shares the array, so the single-launch decode's counters may
+  // hold another call's data: they are cleared first (a fill kernel, capturable)
+  const hmoe::Layer& L = layer->L;
+  if (L.fused_decode && M > 0 && M <= hmoe::kDecodeMaxM && M <= L.max_tokens) {
+    err = hmoe::launch_sync_clear(L, scratch, stream);
+    if (err != hipSuccess) return hip_fail(err, "static scratch counter clear");
+  }
   return hybrid_moe_forward(layer, weights, x, router_logits, M, y, scratch, have, stream);
 }
 
