@@ -108,6 +108,22 @@ __device__ __forceinline__ int seg_index(int lane) {
   return o;
 }
 
+// Byte offset (field * 8) of the NF3 quad table entry for 12-bit field Q (elements 4Q ..
+// 4Q + 3, bits [12 Q, 12 Q + 12) of the 96-bit unit d0 d1 d2): the field shifted to bit 3
+// and masked, one shift (or funnel shift) and one mask.
+template <int Q>
+__device__ __forceinline__ uint32_t nf3_quad_offset(uint32_t d0, uint32_t d1, uint32_t d2) {
+  constexpr uint32_t kMask = 0xFFFu << 3;
+  if constexpr (Q == 0) return (d0 << 3) & kMask;
+  else if constexpr (Q == 1) return (d0 >> 9) & kMask;
+  else if constexpr (Q == 2) return __builtin_amdgcn_alignbit(d1, d0, 21) & kMask;
+  else if constexpr (Q == 3) return (d1 >> 1) & kMask;
+  else if constexpr (Q == 4) return (d1 >> 13) & kMask;
+  else if constexpr (Q == 5) return __builtin_amdgcn_alignbit(d2, d1, 25) & kMask;
+  else if constexpr (Q == 6) return (d2 >> 5) & kMask;
+  else return (d2 >> 17) & kMask;
+}
+
 // Partial dot products of one lane for one row over its KU units. F16 selects the
 // fp16 pair path (W2) over the bf16 one (W13).
 template <int LR, int KU, int NT, bool F16>
@@ -175,7 +191,10 @@ struct RowDot {
       }
     }
   }
-  // NF3: level pairs from the per-lane LDS table, fp16 group scale per 64
+  // NF3 from the per-lane pair table [64 pair fields][64 lanes] (the smaller table, for
+  // kernels whose occupancy the quad table's LDS would limit): fp16 group scale per 64.
+  // Both tables hold the same values and the dot products run in the same order, so the
+  // results are the same bits.
   static __device__ __forceinline__ void nf3(const uint4 (&q)[KU], const uint32_t (&sc)[KU],
                                              const uint32_t* __restrict__ lut_lane,
                                              const uint32_t (&x)[NT][KU][16], float (&acc)[NT]) {
@@ -200,6 +219,41 @@ struct RowDot {
       w[13] = lut_lane[nf3_pair_field<13>(d0, d1, d2) << 6];
       w[14] = lut_lane[nf3_pair_field<14>(d0, d1, d2) << 6];
       w[15] = lut_lane[nf3_pair_field<15>(d0, d1, d2) << 6];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float pp = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pp = dot(w[i], x[t][j][i], pp);
+        acc[t] = __builtin_fmaf(s, pp, acc[t]);
+      }
+    }
+  }
+  // NF3: level quads from the LDS table, fp16 group scale per 64. Each 12-bit field (four
+  // codes) gives its entry's byte offset in a shift and a mask; the entry holds the
+  // quad's two level pairs.
+  static __device__ __forceinline__ void nf3(const uint4 (&q)[KU], const uint32_t (&sc)[KU],
+                                             const uint2* __restrict__ qlut,
+                                             const uint32_t (&x)[NT][KU][16], float (&acc)[NT]) {
+    const char* base = reinterpret_cast<const char*>(qlut);
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+      const uint32_t d0 = q[j].x, d1 = q[j].y, d2 = q[j].z;
+      const float s = fp16_to_f32(sc[j]);
+      uint32_t w[16];
+      auto quad = [&](auto Q) {
+        constexpr int qi = decltype(Q)::value;
+        const uint2 v = *reinterpret_cast<const uint2*>(base + nf3_quad_offset<qi>(d0, d1, d2));
+        w[2 * qi] = v.x;
+        w[2 * qi + 1] = v.y;
+      };
+      quad(std::integral_constant<int, 0>{});
+      quad(std::integral_constant<int, 1>{});
+      quad(std::integral_constant<int, 2>{});
+      quad(std::integral_constant<int, 3>{});
+      quad(std::integral_constant<int, 4>{});
+      quad(std::integral_constant<int, 5>{});
+      quad(std::integral_constant<int, 6>{});
+      quad(std::integral_constant<int, 7>{});
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         float pp = 0.0f;
@@ -272,13 +326,13 @@ __device__ __forceinline__ void load_row(const GemvArgs& a, size_t grow, int c, 
   }
 }
 
-template <int LR, int KU, int NT, bool F16, int FMT>
+template <int LR, int KU, int NT, bool F16, int FMT, typename TAB>
 __device__ __forceinline__ void row_dot(const uint4 (&q)[KU], const uint32_t (&sc)[KU],
-                                        const uint32_t* lut_lane,
+                                        const TAB* qlut,
                                         const uint32_t (&x)[NT][KU][16], float (&acc)[NT]) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-  if constexpr (FMT == kFmtNf3) RowDot<LR, KU, NT, F16>::nf3(q, sc, lut_lane, x, acc);
+  if constexpr (FMT == kFmtNf3) RowDot<LR, KU, NT, F16>::nf3(q, sc, qlut, x, acc);
   else if constexpr (FMT == kFmtNvfp4) RowDot<LR, KU, NT, F16>::nvfp4(q, sc, x, acc);
   else RowDot<LR, KU, NT, F16>::mxfp4(q, sc, x, acc);
 }
@@ -312,7 +366,7 @@ __device__ __forceinline__ WaveRange wave_range(int total) {
 // 256 writes fields (t >> 6) + 4m, m = 0..15, of lane t & 63: its low code takes two
 // values and its high code is m >> 1, a constant once the loop is unrolled.
 template <bool F16>
-__device__ __forceinline__ void build_nf3_lut(uint32_t* lut, float c) {
+__device__ __forceinline__ void build_nf3_pair_lut(uint32_t* lut, float c) {
   static_assert(kGemvThreads == 256, "four waves build the table");
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & (kWave - 1);
@@ -323,6 +377,24 @@ __device__ __forceinline__ void build_nf3_lut(uint32_t* lut, float c) {
     const float lo = (m & 1) ? lo1 : lo0;
     lut[(w + 4 * m) * kWave + lane] = F16 ? pack_f16(lo, hi) : pack_bf16(lo, hi);
   }
+}
+
+// Builds the NF3 quad table [4096 quad fields]: entry f holds the 16-bit level pairs of
+// its four codes, (level(f & 7) c, level((f >> 3) & 7) c) and (level((f >> 6) & 7) c,
+// level(f >> 9) c), bf16 or fp16 (the low half holds the lower element). Thread t of the
+// 256 writes entries t + 256 i, i = 0..15: their first pair is the same for every i,
+// their second pair is that of field (t >> 6) + 4 i.
+template <bool F16>
+__device__ __forceinline__ void build_nf3_lut(uint2* lut, float c) {
+  static_assert(kGemvThreads == 256, "four waves build the table");
+  const int t = threadIdx.x;
+  auto pair = [&](int p) {
+    const float lo = nf3_level((uint32_t)p & 7u) * c, hi = nf3_level((uint32_t)p >> 3) * c;
+    return F16 ? pack_f16(lo, hi) : pack_bf16(lo, hi);
+  };
+  const uint32_t first = pair(t & 63);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lut[t + 256 * i] = make_uint2(first, pair((t >> 6) + 4 * i));
 }
 
 // ---------------------------------------------------------------------------
@@ -414,10 +486,10 @@ __device__ __forceinline__ void w13_load(const GemvArgs& a, int loc, int i0, W13
   }
 }
 
-template <int LR, int KU, int RI, int FMT, bool COH = false>
+template <int LR, int KU, int RI, int FMT, bool COH = false, typename TAB>
 __device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, int slot, float g,
                                             const uint32_t (&x)[1][KU][16],
-                                            const uint32_t* lut_lane, const W13Buf<KU, RI>& b) {
+                                            const TAB* qlut, const W13Buf<KU, RI>& b) {
   constexpr int P = kWave / LR;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % LR;
@@ -426,8 +498,8 @@ __device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, int slot,
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     float ag[1], au[1];
-    row_dot<LR, KU, 1, false, FMT>(b.qg[ri], b.sg[ri], lut_lane, x, ag);
-    row_dot<LR, KU, 1, false, FMT>(b.qu[ri], b.su[ri], lut_lane, x, au);
+    row_dot<LR, KU, 1, false, FMT>(b.qg[ri], b.sg[ri], qlut, x, ag);
+    row_dot<LR, KU, 1, false, FMT>(b.qu[ri], b.su[ri], qlut, x, au);
     vg[ri] = ag[0];
     vu[ri] = au[0];
   }
@@ -443,9 +515,9 @@ __device__ __forceinline__ void w13_compute(const GemvArgs& a, int i0, int slot,
 
 // Chunks [c0, end) of one pass (chunk `first` is the expert's pair 0). A holds
 // chunk c0 on entry when a_loaded.
-template <int LR, int KU, int RI, int FMT, bool COH = false>
+template <int LR, int KU, int RI, int FMT, bool COH = false, typename TAB>
 __device__ __forceinline__ void w13_pass(const GemvArgs& a, const PassInfo& pi, int c0, int end,
-                                         int first, float g, const uint32_t* lut_lane,
+                                         int first, float g, const TAB* qlut,
                                          W13Buf<KU, RI>& A, W13Buf<KU, RI>& B, bool a_loaded) {
   constexpr int CH = (kWave / LR) * RI;
   const int c = (threadIdx.x & (kWave - 1)) % LR;
@@ -457,19 +529,19 @@ __device__ __forceinline__ void w13_pass(const GemvArgs& a, const PassInfo& pi, 
   // so that the wait counts before each compute are the same on every path
   while (cc < end) {
     w13_load<LR, KU, RI, FMT>(a, pi.loc, (min(cc + 1, end - 1) - first) * CH, B);
-    w13_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
+    w13_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, A);
     if (++cc >= end) break;
     w13_load<LR, KU, RI, FMT>(a, pi.loc, (min(cc + 1, end - 1) - first) * CH, A);
-    w13_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
+    w13_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, B);
     ++cc;
   }
 }
 
 template <int LR, int KU, int RI>
 __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
-  __shared__ uint32_t lut[64 * kWave];  // [pair field][lane]: bf16 pair of scaled NF3 levels
+  __shared__ uint2 lut[4096];  // [quad field]: bf16 pairs of scaled NF3 levels
   constexpr int CH = (kWave / LR) * RI;  // pairs per chunk
-  const uint32_t* lut_lane = lut + (threadIdx.x & (kWave - 1));
+  const uint2* qlut = lut;
   const int per = a.out_units / CH;      // chunks per pass
   const WaveRange wr = wave_range<false>(a.npass * per);
   // the first chunk's weights are requested before the table is built
@@ -503,7 +575,7 @@ __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
       const float g = pi.nf3 ? 1.0f / kNF3TableScaleBf16
                              : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[pi.loc] : 1.0f);
       with_format(a, pi, [&](auto f) {
-        w13_pass<LR, KU, RI, decltype(f)::value>(a, pi, ch, p_end, p * per, g, lut_lane, A, B,
+        w13_pass<LR, KU, RI, decltype(f)::value>(a, pi, ch, p_end, p * per, g, qlut, A, B,
                                                  first);
       });
     }
@@ -591,10 +663,10 @@ __device__ __forceinline__ void w2_load(const GemvArgs& a, int loc, int n0, W2Bu
     load_row<LR, KU, FMT>(a, (size_t)loc * a.rows + n0 + ri * P + rw, c, b.q[ri], b.sc[ri]);
 }
 
-template <int LR, int KU, int RI, int FMT, bool COH = false>
+template <int LR, int KU, int RI, int FMT, bool COH = false, typename TAB>
 __device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, int slot, float g,
                                            const uint32_t (&x)[1][KU][16],
-                                           const uint32_t* lut_lane, const W2Buf<KU, RI>& b) {
+                                           const TAB* qlut, const W2Buf<KU, RI>& b) {
   constexpr int P = kWave / LR;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % LR;
@@ -603,7 +675,7 @@ __device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, int slot, 
 #pragma unroll
   for (int ri = 0; ri < RI; ++ri) {
     float acc[1];
-    row_dot<LR, KU, 1, true, FMT>(b.q[ri], b.sc[ri], lut_lane, x, acc);
+    row_dot<LR, KU, 1, true, FMT>(b.q[ri], b.sc[ri], qlut, x, acc);
     v[ri] = acc[0];
   }
   const float sum = seg_reduce<RI, LR>(v);
@@ -615,9 +687,9 @@ __device__ __forceinline__ void w2_compute(const GemvArgs& a, int n0, int slot, 
   }
 }
 
-template <int LR, int KU, int RI, int FMT, bool COH = false>
+template <int LR, int KU, int RI, int FMT, bool COH = false, typename TAB>
 __device__ __forceinline__ void w2_pass(const GemvArgs& a, const PassInfo& pi, int c0, int end,
-                                        int first, float gt, const uint32_t* lut_lane,
+                                        int first, float gt, const TAB* qlut,
                                         uint32_t* hs, W2Buf<KU, RI>& A, W2Buf<KU, RI>& B,
                                         bool a_loaded) {
   constexpr int CH = (kWave / LR) * RI;
@@ -628,10 +700,10 @@ __device__ __forceinline__ void w2_pass(const GemvArgs& a, const PassInfo& pi, i
   const float g = __builtin_ldexpf(gt, stage_h<LR, KU, COH>(a, pi.slot, hs, c, x));
   while (cc < end) {
     if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, B);
-    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, A);
+    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, A);
     if (++cc >= end) break;
     if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, A);
-    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, lut_lane, B);
+    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, B);
     ++cc;
   }
 }
@@ -639,11 +711,11 @@ __device__ __forceinline__ void w2_pass(const GemvArgs& a, const PassInfo& pi, i
 // dynamic LDS: one staged h row (K fp16) per wave
 template <int LR, int KU, int RI>
 __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
-  __shared__ uint32_t lut[64 * kWave];  // [pair field][lane]: fp16 pair of scaled NF3 levels
+  __shared__ uint2 lut[4096];  // [quad field]: fp16 pairs of scaled NF3 levels
   extern __shared__ uint32_t h_stage[];
   constexpr int CH = (kWave / LR) * RI;  // rows per chunk
   constexpr int KD = 16 * LR * KU;        // dwords per staged row (K / 2)
-  const uint32_t* lut_lane = lut + (threadIdx.x & (kWave - 1));
+  const uint2* qlut = lut;
   uint32_t* hs = h_stage + KD * (threadIdx.x >> 6);
   const int per = a.out_units / CH;
   const WaveRange wr = wave_range<true>(a.npass * per);
@@ -677,7 +749,7 @@ __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
       const float gt = pi.nf3 ? 1.0f / kNF3TableScaleF16
                               : (a.kept_fmt == HMOE_KEPT_NVFP4 ? a.kg[pi.loc] : 1.0f);
       with_format(a, pi, [&](auto f) {
-        w2_pass<LR, KU, RI, decltype(f)::value>(a, pi, ch, p_end, p * per, gt, lut_lane, hs, A,
+        w2_pass<LR, KU, RI, decltype(f)::value>(a, pi, ch, p_end, p * per, gt, qlut, hs, A,
                                                 B, first);
       });
     }
@@ -964,16 +1036,24 @@ __device__ __forceinline__ void fused_combine(const FusedArgs& f, int t, int g, 
   f.y[(size_t)t * H + n] = (uint16_t)(pack_bf16(acc, 0.0f) & 0xFFFFu);
 }
 
-template <int LR13, int KU13, int RI13, int LR2, int KU2, int RI2>
+// QUAD: NF3 through the quad tables (two 32 KB tables); otherwise the per-lane pair tables
+// (two 16 KB tables), for tilings whose register use leaves room for a third block per
+// CU that the larger tables would take away. Same values, same bits either way.
+template <int LR13, int KU13, int RI13, int LR2, int KU2, int RI2, bool QUAD>
 __global__ __launch_bounds__(kGemvThreads) void decode_fused_kernel(FusedArgs f, TierMask tm) {
   constexpr int CH13 = (kWave / LR13) * RI13;
   constexpr int CH2 = (kWave / LR2) * RI2;
   constexpr int KD2 = 16 * LR2 * KU2;          // dwords of one staged h row
   static_assert(kCombRows % CH2 == 0, "combine groups hold whole W2 chunks");
-  struct Luts {
+  struct QuadLuts {
+    uint2 w13[4096];   // [quad field]: bf16 pairs of scaled NF3 levels
+    uint2 w2[4096];    // the same in fp16
+  };
+  struct PairLuts {
     uint32_t w13[64 * kWave];   // [pair field][lane]: bf16 pairs of scaled NF3 levels
     uint32_t w2[64 * kWave];    // the same in fp16
   };
+  using Luts = std::conditional_t<QUAD, QuadLuts, PairLuts>;
   union Big {
     Luts luts;
     GroupSmem group;
@@ -1009,8 +1089,13 @@ __global__ __launch_bounds__(kGemvThreads) void decode_fused_kernel(FusedArgs f,
       const int ta = wv, tb = wv + kGemvWaves;
       if (ta < f.M) route_fetch<NV>(f.logits + (size_t)ta * f.E, f.E, lane, xa);
       if (tb < f.M) route_fetch<NV>(f.logits + (size_t)tb * f.E, f.E, lane, xb);
-      build_nf3_lut<false>(big.luts.w13, kNF3TableScaleBf16);
-      build_nf3_lut<true>(big.luts.w2, kNF3TableScaleF16);
+      if constexpr (QUAD) {
+        build_nf3_lut<false>(big.luts.w13, kNF3TableScaleBf16);
+        build_nf3_lut<true>(big.luts.w2, kNF3TableScaleF16);
+      } else {
+        build_nf3_pair_lut<false>(big.luts.w13, kNF3TableScaleBf16);
+        build_nf3_pair_lut<true>(big.luts.w2, kNF3TableScaleF16);
+      }
       float wl;
       if (ta < f.M) {
         const int e = route_rank<NV>(xa, f.E, f.k, lane, &wl);
@@ -1028,8 +1113,8 @@ __global__ __launch_bounds__(kGemvThreads) void decode_fused_kernel(FusedArgs f,
       }
     });
     __syncthreads();
-    const uint32_t* lut13 = big.luts.w13 + lane;
-    const uint32_t* lut2 = big.luts.w2 + lane;
+    const auto* lut13 = QUAD ? big.luts.w13 : big.luts.w13 + lane;
+    const auto* lut2 = QUAD ? big.luts.w2 : big.luts.w2 + lane;
     const int npass = f.M * f.k;
 
     // ---- W13 + SwiGLU: run gw of the flat range (blocks first)
@@ -1295,19 +1380,21 @@ hipError_t launch_decode(const Layer& L, const hmoe_weights& W, const uint16_t* 
 // instantiated for; other layer shapes run the four-launch path
 typedef void (*FusedFn)(FusedArgs, TierMask);
 
+// QUAD (last field): the tiling's registers already hold it to two blocks per CU, which
+// the quad tables' LDS allows; the others keep the pair tables and their third block
 static FusedFn pick_fused(const GemvTiling& a, const GemvTiling& b) {
-#define HMOE_FUSED_CASE(L1, K1, R1, L2, K2, R2)                                        \
+#define HMOE_FUSED_CASE(L1, K1, R1, L2, K2, R2, Q)                                     \
   if (a.lr == L1 && a.ku == K1 && a.ri == R1 && b.lr == L2 && b.ku == K2 && b.ri == R2) \
-    return decode_fused_kernel<L1, K1, R1, L2, K2, R2>;
-  HMOE_FUSED_CASE(8, 1, 2, 4, 1, 2)     // H = 256, I = 128
-  HMOE_FUSED_CASE(4, 3, 1, 8, 1, 2)     // H = 384, I = 256
-  HMOE_FUSED_CASE(16, 1, 2, 8, 1, 2)    // H = 512, I = 256
-  HMOE_FUSED_CASE(32, 1, 2, 16, 1, 2)   // H = 1024, I = 512
-  HMOE_FUSED_CASE(64, 1, 2, 8, 3, 1)    // H = 2048, I = 768 (Qwen3-MoE-shaped)
-  HMOE_FUSED_CASE(64, 3, 1, 64, 1, 2)   // H = 6144, I = 2048 (GLM-class)
-  HMOE_FUSED_CASE(64, 2, 2, 32, 3, 1)   // H = 4096, I = 1536
-  HMOE_FUSED_CASE(64, 2, 2, 64, 1, 2)   // H = 4096, I = 2048
-  HMOE_FUSED_CASE(64, 1, 2, 16, 3, 1)   // H = 2048, I = 1536
+    return decode_fused_kernel<L1, K1, R1, L2, K2, R2, Q>;
+  HMOE_FUSED_CASE(8, 1, 2, 4, 1, 2, false)     // H = 256, I = 128
+  HMOE_FUSED_CASE(4, 3, 1, 8, 1, 2, false)     // H = 384, I = 256
+  HMOE_FUSED_CASE(16, 1, 2, 8, 1, 2, false)    // H = 512, I = 256
+  HMOE_FUSED_CASE(32, 1, 2, 16, 1, 2, false)   // H = 1024, I = 512
+  HMOE_FUSED_CASE(64, 1, 2, 8, 3, 1, true)     // H = 2048, I = 768 (Qwen3-MoE-shaped)
+  HMOE_FUSED_CASE(64, 3, 1, 64, 1, 2, false)   // H = 6144, I = 2048 (GLM-class)
+  HMOE_FUSED_CASE(64, 2, 2, 32, 3, 1, true)    // H = 4096, I = 1536
+  HMOE_FUSED_CASE(64, 2, 2, 64, 1, 2, false)   // H = 4096, I = 2048
+  HMOE_FUSED_CASE(64, 1, 2, 16, 3, 1, true)    // H = 2048, I = 1536
 #undef HMOE_FUSED_CASE
   return nullptr;
 }
