@@ -382,19 +382,36 @@ __device__ __forceinline__ void build_nf3_pair_lut(uint32_t* lut, float c) {
 // Builds the NF3 quad table [4096 quad fields]: entry f holds the 16-bit level pairs of
 // its four codes, (level(f & 7) c, level((f >> 3) & 7) c) and (level((f >> 6) & 7) c,
 // level(f >> 9) c), bf16 or fp16 (the low half holds the lower element). Thread t of the
-// 256 writes entries t + 256 i, i = 0..15: their first pair is the same for every i,
-// their second pair is that of field (t >> 6) + 4 i.
+// 256 writes entries t + 256 i, i = 0..15: their first pair is that of field t & 63, their
+// second pair that of field w + 4 i, w = t >> 6 (the same for the whole wave). Each lane
+// computes one pair (field = lane) and puts it in its wave's list at (lane & 3) * 16 +
+// (lane >> 2), so the sixteen second pairs of wave w are the list's w-th 64 bytes, read
+// back as four broadcast 16-byte loads: the level selects run once per lane instead of
+// once per entry, which matters at kernel start, where every wave of a CU builds a copy.
 template <bool F16>
 __device__ __forceinline__ void build_nf3_lut(uint2* lut, float c) {
   static_assert(kGemvThreads == 256, "four waves build the table");
+  __shared__ uint32_t pairs_t[kGemvWaves][kWave];
   const int t = threadIdx.x;
-  auto pair = [&](int p) {
-    const float lo = nf3_level((uint32_t)p & 7u) * c, hi = nf3_level((uint32_t)p >> 3) * c;
-    return F16 ? pack_f16(lo, hi) : pack_bf16(lo, hi);
-  };
-  const uint32_t first = pair(t & 63);
+  const int lane = t & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const float lo = nf3_level((uint32_t)lane & 7u) * c, hi = nf3_level((uint32_t)lane >> 3) * c;
+  const uint32_t mine = F16 ? pack_f16(lo, hi) : pack_bf16(lo, hi);
+  pairs_t[w][(lane & 3) * 16 + (lane >> 2)] = mine;
+  // LDS operations of one wave complete in order: the reads below see the writes
+  __builtin_amdgcn_wave_barrier();
+  const uint4* src = reinterpret_cast<const uint4*>(&pairs_t[w][16 * w]);
+  uint32_t p[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lut[t + 256 * i] = make_uint2(first, pair((t >> 6) + 4 * i));
+  for (int v = 0; v < 4; ++v) {
+    const uint4 q = src[v];
+    p[4 * v] = q.x;
+    p[4 * v + 1] = q.y;
+    p[4 * v + 2] = q.z;
+    p[4 * v + 3] = q.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lut[t + 256 * i] = make_uint2(mine, p[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -547,21 +564,18 @@ __global__ __launch_bounds__(kGemvThreads) void w13_gemv_kernel(GemvArgs a) {
   // the first chunk's weights are requested before the table is built
   W13Buf<KU, RI> A, B;
   PassInfo pi{};
-  int4 r_first{}, r_next{};
+  int4 r_next{};
   if (wr.begin < wr.end) {
     const int p = wr.begin / per;
-    r_first = a.pass[p];
+    const int4 r_first = a.pass[p];
     if (p + 1 < a.npass) r_next = a.pass[p + 1];
-  }
-  build_nf3_lut<false>(lut, kNF3TableScaleBf16);
-  if (wr.begin < wr.end) {
-    const int p = wr.begin / per;
     pi = pass_info(a, r_first);
     if (pi.ok)
       with_format(a, pi, [&](auto f) {
         w13_load<LR, KU, RI, decltype(f)::value>(a, pi.loc, (wr.begin - p * per) * CH, A);
       });
   }
+  build_nf3_lut<false>(lut, kNF3TableScaleBf16);
   __syncthreads();
   bool first = true;
   for (int ch = wr.begin; ch < wr.end;) {
@@ -719,23 +733,21 @@ __global__ __launch_bounds__(kGemvThreads) void w2_gemv_kernel(GemvArgs a) {
   uint32_t* hs = h_stage + KD * (threadIdx.x >> 6);
   const int per = a.out_units / CH;
   const WaveRange wr = wave_range<true>(a.npass * per);
+  // the first chunk's weights are requested before the table is built
   W2Buf<KU, RI> A, B;
   PassInfo pi{};
-  int4 r_first{}, r_next{};
+  int4 r_next{};
   if (wr.begin < wr.end) {
     const int p = wr.begin / per;
-    r_first = a.pass[p];
+    const int4 r_first = a.pass[p];
     if (p + 1 < a.npass) r_next = a.pass[p + 1];
-  }
-  build_nf3_lut<true>(lut, kNF3TableScaleF16);
-  if (wr.begin < wr.end) {
-    const int p = wr.begin / per;
     pi = pass_info(a, r_first);
     if (pi.ok)
       with_format(a, pi, [&](auto f) {
         w2_load<LR, KU, RI, decltype(f)::value>(a, pi.loc, (wr.begin - p * per) * CH, A);
       });
   }
+  build_nf3_lut<true>(lut, kNF3TableScaleF16);
   __syncthreads();
   bool first = true;
   for (int ch = wr.begin; ch < wr.end;) {
