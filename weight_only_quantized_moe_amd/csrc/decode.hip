@@ -414,6 +414,99 @@ __device__ __forceinline__ void build_nf3_lut(uint2* lut, float c) {
   for (int i = 0; i < 16; ++i) lut[t + 256 * i] = make_uint2(mine, p[i]);
 }
 
+// The routing of every token, shared by a block's waves through LDS: slot s = t * k + j
+// routes to expert ids[s] with weight w[s]; the tier map's words and, for each word, the
+// NF3 experts below it (so a pass's tier code is two LDS reads, not a loop over the
+// kernel argument's words).
+struct BlockRoute {
+  int32_t ids[kDecodeMaxM * kMaxTopK];
+  float w[kDecodeMaxM * kMaxTopK];
+  uint32_t tier_w[kMaxExperts / 32];
+  int32_t tier_below[kMaxExperts / 32];
+};
+
+// tier_code (bit 16: NF3 tier; low bits: index within the tier) from the block's copy
+__device__ __forceinline__ int block_tier_code(const BlockRoute& br, int e) {
+  const uint32_t w = br.tier_w[e >> 5];
+  const int below = br.tier_below[e >> 5] + __popc(w & ((1u << (e & 31)) - 1u));
+  return ((w >> (e & 31)) & 1u) ? ((1 << 16) | below) : (e - below);
+}
+
+// calls f with NV (logits per lane for E experts) as a compile-time constant
+template <typename F>
+__device__ __forceinline__ void with_nv(int E, F&& f) {
+  if (E <= 64) f(std::integral_constant<int, 1>{});
+  else if (E <= 128) f(std::integral_constant<int, 2>{});
+  else if (E <= 256) f(std::integral_constant<int, 4>{});
+  else if (E <= 512) f(std::integral_constant<int, 8>{});
+  else f(std::integral_constant<int, 16>{});
+}
+
+// Pass p (slot p: token p / k) from the block's routing: the same record the routing
+// launch writes to scratch (pass_info), taken from LDS.
+__device__ __forceinline__ PassInfo block_pass(const GemvArgs& a, int k, int p,
+                                               const BlockRoute& br) {
+  const int e = __builtin_amdgcn_readfirstlane(br.ids[p]);
+  const int code = (unsigned)e < (unsigned)a.E ? block_tier_code(br, e) : 0;
+  PassInfo pi;
+  pi.slot = p;
+  pi.token = p / k;
+  pi.nf3 = (code >> 16) != 0;
+  pi.loc = code & 0xFFFF;
+  pi.ok = (unsigned)e < (unsigned)a.E && pi.loc < (pi.nf3 ? a.E3 : a.E4);
+  return pi;
+}
+
+// Every token's routing into the block's LDS (wave w: tokens w and w + 4), the logits
+// rows requested before `between` runs (the level table build), and the tier map's copy.
+template <typename F>
+__device__ __forceinline__ void block_route(const float* __restrict__ logits, int M, int E, int k,
+                                            const TierMask& tm, BlockRoute& br, F&& between) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  if (threadIdx.x == 0) {
+    int below = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / 32; ++i) {
+      br.tier_w[i] = tm.w[i];
+      br.tier_below[i] = below;
+      below += __popc(tm.w[i]);
+    }
+  }
+  with_nv(E, [&](auto nvc) {
+    constexpr int NV = decltype(nvc)::value;
+    const int ta = wv, tb = wv + kGemvWaves;
+    if (tb < M) {
+      // two tokens, their routing steps interleaved
+      float x[2][NV];
+      route_fetch<NV>(logits + (size_t)ta * E, E, lane, x[0]);
+      route_fetch<NV>(logits + (size_t)tb * E, E, lane, x[1]);
+      between();
+      int e[2];
+      float wl[2];
+      route_rank_n<NV, 2>(x, E, k, lane, e, wl);
+      if (lane < k) {
+        br.ids[ta * k + lane] = e[0];
+        br.w[ta * k + lane] = wl[0];
+        br.ids[tb * k + lane] = e[1];
+        br.w[tb * k + lane] = wl[1];
+      }
+    } else {
+      float x[NV];
+      if (ta < M) route_fetch<NV>(logits + (size_t)ta * E, E, lane, x);
+      between();
+      if (ta < M) {
+        float wl;
+        const int e = route_rank<NV>(x, E, k, lane, &wl);
+        if (lane < k) {
+          br.ids[ta * k + lane] = e;
+          br.w[ta * k + lane] = wl;
+        }
+      }
+    }
+  });
+}
+
 // ---------------------------------------------------------------------------
 // W13 + SwiGLU
 // ---------------------------------------------------------------------------
@@ -665,16 +758,24 @@ struct W2Buf {
   uint32_t sc[RI][KU];
 };
 
-template <int LR, int KU, int RI, int FMT>
+// BUF: buffer loads (the chunk's row offset in a scalar register, the lane's offset
+// fixed); otherwise flat loads (the single-launch decode, where they measured faster)
+template <int LR, int KU, int RI, int FMT, bool BUF = true>
 __device__ __forceinline__ void w2_load(const GemvArgs& a, int loc, int n0, W2Buf<KU, RI>& b) {
   constexpr int P = kWave / LR;
   const int lane = threadIdx.x & (kWave - 1);
   const int c = lane % LR;
   const int rw = lane / LR;
-  // flat loads here: buffer loads made the W2 GEMV slower on the GLM-class layer
+  if constexpr (BUF) {
+    const ExpertRsrc r = expert_rsrc<FMT>(a, loc);
 #pragma unroll
-  for (int ri = 0; ri < RI; ++ri)
-    load_row<LR, KU, FMT>(a, (size_t)loc * a.rows + n0 + ri * P + rw, c, b.q[ri], b.sc[ri]);
+    for (int ri = 0; ri < RI; ++ri)
+      load_row_rsrc<LR, KU, FMT>(r, a.K, n0 + ri * P, rw, c, b.q[ri], b.sc[ri]);
+  } else {
+#pragma unroll
+    for (int ri = 0; ri < RI; ++ri)
+      load_row<LR, KU, FMT>(a, (size_t)loc * a.rows + n0 + ri * P + rw, c, b.q[ri], b.sc[ri]);
+  }
 }
 
 template <int LR, int KU, int RI, int FMT, bool COH = false, typename TAB>
@@ -709,16 +810,33 @@ __device__ __forceinline__ void w2_pass(const GemvArgs& a, const PassInfo& pi, i
   constexpr int CH = (kWave / LR) * RI;
   const int c = (threadIdx.x & (kWave - 1)) % LR;
   int cc = c0;
-  if (!a_loaded) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc - first) * CH, A);
+  if (!a_loaded) w2_load<LR, KU, RI, FMT, !COH>(a, pi.loc, (cc - first) * CH, A);
   uint32_t x[1][KU][16];
   const float g = __builtin_ldexpf(gt, stage_h<LR, KU, COH>(a, pi.slot, hs, c, x));
-  while (cc < end) {
-    if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, B);
-    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, A);
-    if (++cc >= end) break;
-    if (cc + 1 < end) w2_load<LR, KU, RI, FMT>(a, pi.loc, (cc + 1 - first) * CH, A);
-    w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, B);
-    ++cc;
+  if constexpr (COH) {
+    // the single-launch decode: the next chunk is loaded only when there is one
+    while (cc < end) {
+      if (cc + 1 < end) w2_load<LR, KU, RI, FMT, false>(a, pi.loc, (cc + 1 - first) * CH, B);
+      w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, A);
+      if (++cc >= end) break;
+      if (cc + 1 < end) w2_load<LR, KU, RI, FMT, false>(a, pi.loc, (cc + 1 - first) * CH, A);
+      w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, B);
+      ++cc;
+    }
+  } else {
+    // as in the W13 pass: the next chunk's loads are issued on every path (the last
+    // chunk repeats itself) and the compiler may not move the current chunk's wait above
+    // them, so each compute waits only for its own chunk
+    while (cc < end) {
+      w2_load<LR, KU, RI, FMT>(a, pi.loc, (min(cc + 1, end - 1) - first) * CH, B);
+      __builtin_amdgcn_sched_barrier(0);
+      w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, A);
+      if (++cc >= end) break;
+      w2_load<LR, KU, RI, FMT>(a, pi.loc, (min(cc + 1, end - 1) - first) * CH, A);
+      __builtin_amdgcn_sched_barrier(0);
+      w2_compute<LR, KU, RI, FMT, COH>(a, (cc - first) * CH, pi.slot, g, x, qlut, B);
+      ++cc;
+    }
   }
 }
 
@@ -973,34 +1091,9 @@ __device__ __forceinline__ void wait_vmem() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// The routing of every token, shared by a block's waves through LDS: slot s = t * k + j
-// routes to expert ids[s] with weight w[s].
-struct BlockRoute {
-  int32_t ids[kDecodeMaxM * kMaxTopK];
-  float w[kDecodeMaxM * kMaxTopK];
-};
-
-// calls f with NV (logits per lane for E experts) as a compile-time constant
-template <typename F>
-__device__ __forceinline__ void with_nv(int E, F&& f) {
-  if (E <= 64) f(std::integral_constant<int, 1>{});
-  else if (E <= 128) f(std::integral_constant<int, 2>{});
-  else if (E <= 256) f(std::integral_constant<int, 4>{});
-  else if (E <= 512) f(std::integral_constant<int, 8>{});
-  else f(std::integral_constant<int, 16>{});
-}
-
 __device__ __forceinline__ PassInfo fused_pass(const FusedArgs& f, const TierMask& tm, int p,
                                                const BlockRoute& br) {
-  const int e = __builtin_amdgcn_readfirstlane(br.ids[p]);
-  const int code = tier_code(tm, e);
-  PassInfo pi;
-  pi.slot = p;
-  pi.token = p / f.k;
-  pi.nf3 = (code >> 16) != 0;
-  pi.loc = code & 0xFFFF;
-  pi.ok = (unsigned)e < (unsigned)f.E && pi.loc < (pi.nf3 ? f.a13.E3 : f.a13.E4);
-  return pi;
+  return block_pass(f.a13, f.k, p, br);
 }
 
 // this wave's run [b, e) of a flat range of n chunks: runs numbered block-major (the
@@ -1093,35 +1186,14 @@ __global__ __launch_bounds__(kGemvThreads) void decode_fused_kernel(FusedArgs f,
     __syncthreads();
     decode_grouping(f.ga, tm, big.group);
   } else {
-    // every token's routing (wave w: tokens w and w + 4), its logits rows requested
-    // before the level tables are built
-    with_nv(f.E, [&](auto nvc) {
-      constexpr int NV = decltype(nvc)::value;
-      float xa[NV], xb[NV];
-      const int ta = wv, tb = wv + kGemvWaves;
-      if (ta < f.M) route_fetch<NV>(f.logits + (size_t)ta * f.E, f.E, lane, xa);
-      if (tb < f.M) route_fetch<NV>(f.logits + (size_t)tb * f.E, f.E, lane, xb);
+    // every token's routing, its logits rows requested before the level tables are built
+    block_route(f.logits, f.M, f.E, f.k, tm, br, [&] {
       if constexpr (QUAD) {
         build_nf3_lut<false>(big.luts.w13, kNF3TableScaleBf16);
         build_nf3_lut<true>(big.luts.w2, kNF3TableScaleF16);
       } else {
         build_nf3_pair_lut<false>(big.luts.w13, kNF3TableScaleBf16);
         build_nf3_pair_lut<true>(big.luts.w2, kNF3TableScaleF16);
-      }
-      float wl;
-      if (ta < f.M) {
-        const int e = route_rank<NV>(xa, f.E, f.k, lane, &wl);
-        if (lane < f.k) {
-          br.ids[ta * f.k + lane] = e;
-          br.w[ta * f.k + lane] = wl;
-        }
-      }
-      if (tb < f.M) {
-        const int e = route_rank<NV>(xb, f.E, f.k, lane, &wl);
-        if (lane < f.k) {
-          br.ids[tb * f.k + lane] = e;
-          br.w[tb * f.k + lane] = wl;
-        }
       }
     });
     __syncthreads();
@@ -1172,7 +1244,7 @@ __global__ __launch_bounds__(kGemvThreads) void decode_fused_kernel(FusedArgs f,
         // the first chunk's weights are requested before the wait for h
         if (pi.ok)
           with_format(f.a2, pi, [&](auto fm) {
-            w2_load<LR2, KU2, RI2, decltype(fm)::value>(f.a2, pi.loc, (ch - p * f.per2) * CH2, A);
+            w2_load<LR2, KU2, RI2, decltype(fm)::value, false>(f.a2, pi.loc, (ch - p * f.per2) * CH2, A);
           });
         wait_h(f, p);
         if (pi.ok) {

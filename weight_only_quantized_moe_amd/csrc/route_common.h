@@ -34,67 +34,112 @@ __device__ __forceinline__ void route_fetch(const float* __restrict__ row, int E
   }
 }
 
-// Top-k of one token's logits by one wave (each lane holds NV >= E / 64 of them, from
-// route_fetch). Experts rank by logit, descending, ties to the lower id; NaN ranks
-// below -inf and -0 ties with +0. Each of the k rounds takes the wave's largest
-// order-preserving 32-bit key (lane maxima, then a butterfly max), the lowest expert id
-// holding it (one ballot per slot), and clears that key, so round r yields rank r.
-// Lane j < k returns the j-th selection and writes its weight to *w_lane (lanes >= k:
-// 0). Weights: softmax over the selected logits, in fp64, rounded once to fp32.
+// Top-k of T tokens' logits by one wave (each lane holds NV >= E / 64 of each row, from
+// route_fetch), the tokens' steps interleaved so that their dependency chains overlap.
+// Experts rank by logit, descending, ties to the lower id; NaN ranks below -inf and -0
+// ties with +0. Each of the k rounds takes the wave's largest order-preserving 32-bit key
+// (lane maxima, then a butterfly max), the lowest expert id holding it (one ballot per
+// slot), and clears that key, so round r yields rank r. Lane j < k gets the j-th
+// selection of token t in sel[t] and its weight in w[t] (lanes >= k: 0). Weights: softmax
+// over the selected logits, in fp64, rounded once to fp32. Every token takes the same
+// operations whatever T is, so the results do not depend on T.
+template <int NV, int T>
+__device__ __forceinline__ void route_rank_n(const float (&x)[T][NV], int E, int k, int lane,
+                                             int (&sel)[T], float (&w)[T]) {
+  uint32_t u[T][NV];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = lane + kWave * i;
+      float v = x[t][i];
+      const bool nan = v != v;
+      v = (v == 0.0f) ? 0.0f : v;    // -0 ties with +0
+      // keys: -inf is 0x007FFFFF, NaN 1 (below every number), padding 0 (never chosen: k <= E)
+      u[t][i] = (e < E) ? (nan ? 1u : order_key(v)) : 0u;
+    }
+  uint32_t sel_key[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    sel[t] = 0;
+    sel_key[t] = 0u;
+  }
+  for (int r = 0; r < k; ++r) {
+    uint32_t m[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      m[t] = u[t][0];
+#pragma unroll
+      for (int i = 1; i < NV; ++i) m[t] = max(m[t], u[t][i]);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) m[t] = max(m[t], xlane_u32<32>(m[t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) m[t] = max(m[t], xlane_u32<16>(m[t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) m[t] = max(m[t], xlane_u32<8>(m[t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) m[t] = max(m[t], xlane_u32<4>(m[t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) m[t] = max(m[t], xlane_u32<2>(m[t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) m[t] = max(m[t], xlane_u32<1>(m[t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      m[t] = __builtin_amdgcn_readfirstlane(m[t]);
+      // the lowest id with key m: slots hold ids 64 i .. 64 i + 63, so the first slot
+      // with a match and its lowest matching lane
+      int id = -1;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const uint64_t b = __ballot(u[t][i] == m[t]);
+        if (id < 0 && b != 0ull) id = kWave * i + (int)__builtin_ctzll(b);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (id == kWave * i + lane) u[t][i] = 0u;
+      if (lane == r) {
+        sel[t] = id;
+        sel_key[t] = m[t];
+      }
+    }
+  }
+  double ex[T], sum[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const float sel_v = key_value(sel_key[t]);
+    const float v0 =
+        __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(sel_v), 0));
+    ex[t] = (lane < k) ? exp((double)sel_v - (double)v0) : 0.0;
+    sum[t] = ex[t];
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) sum[t] += xlane_d<32>(sum[t]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) sum[t] += xlane_d<16>(sum[t]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) sum[t] += xlane_d<8>(sum[t]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) sum[t] += xlane_d<4>(sum[t]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) sum[t] += xlane_d<2>(sum[t]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) sum[t] += xlane_d<1>(sum[t]);
+#pragma unroll
+  for (int t = 0; t < T; ++t) w[t] = lane < k ? (float)(ex[t] / sum[t]) : 0.0f;
+}
+
+// route_rank_n of one token: lane j < k returns the j-th selection and writes its weight
+// to *w_lane
 template <int NV>
 __device__ __forceinline__ int route_rank(const float (&x)[NV], int E, int k, int lane,
                                           float* w_lane) {
-  uint32_t u[NV];
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + kWave * i;
-    float t = x[i];
-    const bool nan = t != t;
-    t = (t == 0.0f) ? 0.0f : t;    // -0 ties with +0
-    // keys: -inf is 0x007FFFFF, NaN 1 (below every number), padding 0 (never chosen: k <= E)
-    u[i] = (e < E) ? (nan ? 1u : order_key(t)) : 0u;
-  }
-  int sel_id = 0;
-  uint32_t sel_key = 0u;
-  for (int r = 0; r < k; ++r) {
-    uint32_t m = u[0];
-#pragma unroll
-    for (int i = 1; i < NV; ++i) m = max(m, u[i]);
-    m = max(m, xlane_u32<32>(m));
-    m = max(m, xlane_u32<16>(m));
-    m = max(m, xlane_u32<8>(m));
-    m = max(m, xlane_u32<4>(m));
-    m = max(m, xlane_u32<2>(m));
-    m = max(m, xlane_u32<1>(m));
-    m = __builtin_amdgcn_readfirstlane(m);
-    // the lowest id with key m: slots hold ids 64 i .. 64 i + 63, so the first slot with
-    // a match and its lowest matching lane
-    int id = -1;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const uint64_t b = __ballot(u[i] == m);
-      if (id < 0 && b != 0ull) id = kWave * i + (int)__builtin_ctzll(b);
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (id == kWave * i + lane) u[i] = 0u;
-    if (lane == r) {
-      sel_id = id;
-      sel_key = m;
-    }
-  }
-  const float sel_v = key_value(sel_key);
-  const float v0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(sel_v), 0));
-  const double ex = (lane < k) ? exp((double)sel_v - (double)v0) : 0.0;
-  double sum = ex;
-  sum += xlane_d<32>(sum);
-  sum += xlane_d<16>(sum);
-  sum += xlane_d<8>(sum);
-  sum += xlane_d<4>(sum);
-  sum += xlane_d<2>(sum);
-  sum += xlane_d<1>(sum);
-  *w_lane = lane < k ? (float)(ex / sum) : 0.0f;
-  return sel_id;
+  const float (&x1)[1][NV] = *reinterpret_cast<const float (*)[1][NV]>(&x);
+  int sel[1];
+  float w[1];
+  route_rank_n<NV, 1>(x1, E, k, lane, sel, w);
+  *w_lane = w[0];
+  return sel[0];
 }
 
 template <int NV>
