@@ -29,6 +29,7 @@ struct ScratchPlan {
   size_t a_counts = 0;                     // int32 [E] slot counts per expert
   size_t a_slots[2] = {0, 0}, a_bexp[2] = {0, 0}, a_eoff[2] = {0, 0}, a_npad[2] = {0, 0};
   size_t h_pre = 0, o_pre = 0, x16_pre = 0, xe_pre = 0;
+  size_t pf_fac = 0;                       // fp32 [cap0 + cap1]: W2 output factor per h row
   size_t mx_xq = 0, mx_xs = 0, mx_h32 = 0, mx_hq = 0, mx_hs = 0;   // W4A4 kept tier
   size_t total = 0;
 };

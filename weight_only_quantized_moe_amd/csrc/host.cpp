@@ -74,11 +74,13 @@ void plan_scratch(hmoe::Layer& L) {
     P.o_pre = take(mk * L.H * 4);
     P.x16_pre = take((size_t)L.max_tokens * L.H * 2);
     P.xe_pre = take((size_t)L.max_tokens * 4);
+    P.pf_fac = take((size_t)(L.cap[0] + L.cap[1]) * 4);
   } else {
     P.h_pre = take(0);
     P.o_pre = take(0);
     P.x16_pre = take(0);
     P.xe_pre = take(0);
+    P.pf_fac = take(0);
   }
   if (L.act_format == HMOE_ACT_MXFP4) {
     P.mx_xq = take((size_t)L.max_tokens * L.H / 2);

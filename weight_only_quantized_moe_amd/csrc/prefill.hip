@@ -96,7 +96,9 @@ struct PrefillArgs {
   int I, H;
   uint16_t* h_out;     // W13: fp16 [cap0 + cap1, I]
   float* o_out;        // W2: fp32 [nslot, H]
-  const float* topk_w;
+  const float* topk_w; // W13: [nslot] routing weights
+  float* row_fac;      // [cap0 + cap1]: the W2 output factor of each h row (routing weight
+                       // times 2^he, 0 for padding), written by W13's first column tile
 };
 
 enum : int { kPfNvfp4 = 0, kPfMxfp4 = 1, kPfNf3 = 2 };
@@ -140,6 +142,9 @@ struct GemmSmem {
   __attribute__((aligned(16))) uint16_t Bs[2][kBN][kBK];
   uint32_t lut[64 * 32];  // NF3: fp16 pairs of scaled levels, [pair field][lane % 32]
   int sRef[kBN];          // MXFP4: largest E8M0 byte; NF3: largest fp16 scale exponent
+  int rowSlot[BM];        // the epilogue's per-row data, loaded at the block's start:
+  int rowE[BM];           //   slot, W13: the token's x exponent,
+  float rowF[BM];         //   W2: the row's output factor
 };
 
 // NVFP4 16-element block (two code words) -> 8 fp16 pairs, exact (see the header).
@@ -463,7 +468,23 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int r0
     else sw = from_x ? w.sx : w.sy;
     store_w(buf, e, q, sw);
   };
-  __syncthreads();  // table, reference exponents
+  // the epilogue's per-row data, requested behind the first loads so that its latency
+  // overlaps theirs instead of adding to the block's end (W13's first column tile also
+  // writes the rows' W2 output factors)
+  if (tid < BM) {
+    const int slot = bslots[tid];
+    sm.rowSlot[tid] = slot;
+    if constexpr (W13) {
+      const bool real = (unsigned)slot < (unsigned)a.nslot;
+      const int e = real ? a.xe[slot / a.k] : 0;
+      sm.rowE[tid] = e;
+      if (tile == 0)
+        a.row_fac[hbase + tid] = real ? __builtin_ldexpf(a.topk_w[slot], h_exponent(e)) : 0.0f;
+    } else {
+      sm.rowF[tid] = a.row_fac[hbase + tid];
+    }
+  }
+  __syncthreads();  // table, reference exponents, row data
   store_a(0, av[0]);
   unit_store(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
              std::true_type{}, pr[0]);
@@ -530,11 +551,11 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int r0
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = (wm * MT + mt) * 16 + 4 * g + q;
-        const int slot = bslots[m];
+        const int slot = sm.rowSlot[m];
         if (W13) {
           // x was scaled by 2^-e, h is stored times 2^-he
           const bool real = (unsigned)slot < (unsigned)a.nslot;
-          const int e = real ? a.xe[slot / a.k] : 0;
+          const int e = sm.rowE[m];
           const float xs = real ? __builtin_ldexpf(1.0f, e) : 0.0f;
           const float gate = acc[mt][nt][q] * gf * xs;
           const float up = acc[mt][nt + NT / 2][q] * uf * xs;
@@ -542,9 +563,9 @@ __device__ __forceinline__ void gemm_tile(const PrefillArgs& a, int tier, int r0
           const float h = fminf(fmaxf(hv, -65504.0f), 65504.0f);
           a.h_out[(hbase + m) * a.I + n] = (uint16_t)(pack_f16(h, 0.0f) & 0xFFFFu);
         } else {
+          // factor = w * 2^he exactly, so this is the rounded (acc * gf * w) scaled by 2^he
           if ((unsigned)slot < (unsigned)a.nslot)
-            a.o_out[(size_t)slot * a.H + n] =
-                __builtin_ldexpf(acc[mt][nt][q] * gf * a.topk_w[slot], h_exponent(a.xe[slot / a.k]));
+            a.o_out[(size_t)slot * a.H + n] = acc[mt][nt][q] * gf * sm.rowF[m];
         }
       }
     }
@@ -784,6 +805,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
   a.H = L.H;
   uint16_t* h = reinterpret_cast<uint16_t*>(base + P.h_pre);
   float* o = reinterpret_cast<float*>(base + P.o_pre);
+  a.row_fac = reinterpret_cast<float*>(base + P.pf_fac);
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base + P.x16_pre);
   int32_t* xe = reinterpret_cast<int32_t*>(base + P.xe_pre);
   const int nblk = a.nblk0 + a.nblk1;
@@ -796,6 +818,7 @@ hipError_t launch_prefill(const Layer& L, const hmoe_weights& W, const uint16_t*
     b.act = x16;
     b.xe = xe;
     b.h_out = h;
+    b.topk_w = w;
     b.ntile = L.I / (kBN / 2);
     b.vec_scales = vec_scales_ok(b);
     return launch_gemm<true>(L, W, M, scratch, b, nblk > 0 ? gemm_grid(nblk, b.ntile) : 0u, nf3_only, s);
