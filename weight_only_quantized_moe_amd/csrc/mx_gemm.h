@@ -32,6 +32,8 @@ struct MxArgs {
   float* h_out;         // W13: fp32 [cap_kept, I]
   float* o_out;         // W2: fp32 [nslot, H]
   const float* topk_w;
+  float* row_fac;       // [cap_kept]: each align row's routing weight (0 for padding),
+                        // written by W13's first column tile, read by W2
 };
 
 // column tiles of a kept-tier W4A4 GEMM: W13 64 h columns per tile, W2 128 outputs
@@ -104,6 +106,22 @@ __device__ __forceinline__ void mx_gemm_tile(const MxArgs& a, int blk, int tile)
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // W2: the epilogue's rows (slot and routing weight), requested now so that their
+  // latency hides under the K loop instead of adding to the tile's end (up to 64-row
+  // tiles; the 128-row tile has no registers to spare and loads them at the end)
+  constexpr bool PRE = !W13 && MT <= 2;
+  int eslot[PRE ? MT : 1][4];
+  float efac[PRE ? MT : 1][4];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = (wm * MT + mt) * 16 + 4 * g + q;
+        eslot[mt][q] = a.slots[r0 + m];
+        efac[mt][q] = a.row_fac[r0 + m];
+      }
+  }
 
   struct Frag {
     uint4 aq[MT], bq[NT];
@@ -227,10 +245,21 @@ __device__ __forceinline__ void mx_gemm_tile(const MxArgs& a, int blk, int tile)
           const float gate = acc[mt][nt][q], up = acc[mt][nt + NT / 2][q];
           a.h_out[(size_t)(r0 + m) * a.I + n] = silu(gate) * up;
         } else {
-          const int slot = a.slots[r0 + m];
+          const int slot = PRE ? eslot[PRE ? mt : 0][q] : a.slots[r0 + m];
+          const float fac = PRE ? efac[PRE ? mt : 0][q] : a.row_fac[r0 + m];
           if ((unsigned)slot < (unsigned)a.nslot)
-            a.o_out[(size_t)slot * a.H + n] = acc[mt][nt][q] * a.topk_w[slot];
+            a.o_out[(size_t)slot * a.H + n] = acc[mt][nt][q] * fac;
         }
+      }
+    }
+  }
+  // W13's first column tile: the rows' routing weights for the W2 epilogue (at the end,
+  // where the two dependent loads delay only this one tile of the align block)
+  if constexpr (W13) {
+    if (tile == 0) {
+      for (int t = threadIdx.x; t < BM; t += kMxThreads) {
+        const int slot = a.slots[r0 + t];
+        a.row_fac[r0 + t] = (unsigned)slot < (unsigned)a.nslot ? a.topk_w[slot] : 0.0f;
       }
     }
   }

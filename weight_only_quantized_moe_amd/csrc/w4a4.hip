@@ -110,6 +110,8 @@ MxArgs mx_args(const Layer& L, const hmoe_weights& W, int M, void* scratch, int 
   a.E4 = L.E4;
   a.I = L.I;
   a.H = L.H;
+  a.topk_w = reinterpret_cast<const float*>(base + P.topk_w);
+  a.row_fac = reinterpret_cast<float*>(base + P.pf_fac);  // the kept tier's rows [0, cap0)
   if (stage == HMOE_STAGE_W13) {
     a.wq = W.kept_w13_q; a.ws = W.kept_w13_s;
     a.rows_w = 2 * L.I; a.K = L.H;
@@ -122,7 +124,6 @@ MxArgs mx_args(const Layer& L, const hmoe_weights& W, int M, void* scratch, int 
     a.aq = reinterpret_cast<const uint8_t*>(base + P.mx_hq);
     a.as = reinterpret_cast<const uint8_t*>(base + P.mx_hs);
     a.o_out = reinterpret_cast<float*>(base + P.o_pre);
-    a.topk_w = reinterpret_cast<const float*>(base + P.topk_w);
   }
   return a;
 }
