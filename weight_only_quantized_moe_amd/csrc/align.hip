@@ -13,6 +13,9 @@ namespace hmoe {
 
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
+// slot ids each lane requests at once (16 steps of 64 slots): the counting and placing
+// loops wait for one load latency per 16 steps, not per step
+constexpr int kAlignBatch = 16;
 // s_waitcnt operand waiting for LDS only (gfx9 fields: vmcnt 63, expcnt 7, lgkmcnt 0):
 // the placement loop orders its position reads and counter updates in LDS but leaves
 // its global stores of slot ids in flight
@@ -56,11 +59,20 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
   }
   for (int i = tid; i < kAlignWaves * kMaxExperts; i += kAlignThreads) (&s_w[0][0])[i] = 0;
   __syncthreads();
-  for (int s = c0 + lane; s < c1; s += kWave) {
-    const int e = a.ids[s];
-    if ((unsigned)e < (unsigned)a.E) {  // ids outside [0, E) are dropped
-      atomicAdd(&s_cnt[e], 1);
-      atomicAdd(&s_w[wave][e], 1);
+  for (int b0 = c0; b0 < c1; b0 += kAlignBatch * kWave) {
+    int ev[kAlignBatch];
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      const int s = b0 + i * kWave + lane;
+      ev[i] = s < c1 ? a.ids[s] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      const int e = ev[i];
+      if ((unsigned)e < (unsigned)a.E) {  // ids outside [0, E) are dropped
+        atomicAdd(&s_cnt[e], 1);
+        atomicAdd(&s_w[wave][e], 1);
+      }
     }
   }
   __syncthreads();
@@ -114,29 +126,40 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(AlignArgs a, TierM
   // equal experts inside the step with ballots over the id bits
   int idbits = 1;
   while ((1 << idbits) < a.E) ++idbits;
-  for (int base = c0; base < c1; base += kWave) {
-    const int s = base + lane;
-    const int e0 = s < c1 ? a.ids[s] : -1;
-    const bool valid = (unsigned)e0 < (unsigned)a.E;
-    const int e = valid ? e0 : 0;
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < idbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
+  for (int b0 = c0; b0 < c1; b0 += kAlignBatch * kWave) {
+    int ev[kAlignBatch];
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      const int s = b0 + i * kWave + lane;
+      ev[i] = s < c1 ? a.ids[s] : -1;
     }
-    const int rank = __popcll(m & ((1ull << lane) - 1ull));
-    const int cnt = __popcll(m);
-    int pos = 0;
-    if (valid) pos = s_w[wave][e] + rank;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
-    if (valid) {
-      a.slots[s_tc[e] >> 16][pos] = s;
-      if (rank == cnt - 1) s_w[wave][e] += cnt;
+#pragma unroll
+    for (int i = 0; i < kAlignBatch; ++i) {
+      const int base = b0 + i * kWave;
+      if (base >= c1) break;
+      const int s = base + lane;
+      const int e0 = ev[i];
+      const bool valid = (unsigned)e0 < (unsigned)a.E;
+      const int e = valid ? e0 : 0;
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < idbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      const int rank = __popcll(m & ((1ull << lane) - 1ull));
+      const int cnt = __popcll(m);
+      int pos = 0;
+      if (valid) pos = s_w[wave][e] + rank;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
+      if (valid) {
+        a.slots[s_tc[e] >> 16][pos] = s;
+        if (rank == cnt - 1) s_w[wave][e] += cnt;
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(kWaitLdsOnly);
   }
 }
 
