@@ -168,6 +168,9 @@ def test_decode_grouping_bit_exact(hm, M):
 @pytest.mark.parametrize("E,k,M,bm,n_kept", [
     (8, 2, 9, 16, 4), (8, 2, 100, 32, 4), (256, 8, 64, 32, 64), (256, 8, 4096, 32, 64),
     (256, 8, 512, 128, 64), (128, 8, 300, 64, 32), (256, 8, 700, 16, None), (64, 4, 1, 64, 16),
+    # 40,000 slots: 2,560 per wave, two and a half batches of 16 steps, the last wave's
+    # chunk ending inside its second batch
+    (256, 8, 5000, 64, 64),
 ])
 def test_align_bit_exact(hm, E, k, M, bm, n_kept):
     torch = torch_mod()
